@@ -1,0 +1,37 @@
+"""CPU oracle for the packed ARCHead LM-head -- TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, obviously-correct CPU implementation of what
+the packed ARCHead head computes, written from the ARCHead paper
+("Activation-Metric Residual Correction for LLM Output Heads", sections
+3.1-3.3, equations 1-10).  It exists to check the HIP path.  Only the test
+suite, the smoke entry point and the CPU-baseline leg of the benchmark may
+import it; the product path (the C-ABI library and its Python binding) never
+does, and there is no fallback from the product path into this code.
+
+It shares no code with the HIP path: its own unpacking of the canonical byte
+layout, its own fp16/bf16 decoding, its own quantiser and its own fp64
+arithmetic.  Floating point is fp64 throughout.
+
+Modules
+-------
+quant    symmetric b-bit quantiser with fp16 scales (eq 3 "Q_b", section 3.2;
+         INT8 correction factors, text after eq 7)
+layout   canonical byte layout: R4 nibble packing, fp16 / bf16 decoding,
+         state-dict byte accounting (eq 10)
+forward  dense fp64 W_hat (eq 6) and logits (eq 7), first-index argmax
+packer   tiny-head construction (eqs 2-5): damped metric, core, SC4 residual,
+         activation-metric correction, INT8 factors
+naive    ctypes loader for naive.c, an independent triple-loop forward in C
+
+Parity pins (what each function is checked against, in tests/):
+  quant   -- closed-form bounds |x - s q| <= s/2, ranges, idempotence, and
+             hand-worked examples in tests/golden/quant_examples.txt
+  layout  -- round trip, hand-packed bytes in tests/golden/r4_nibbles.txt,
+             eq 10 byte counts against the paper's 1187 MiB BF16 Qwen head
+  forward -- the independent C triple loop, one-hot closed forms, special
+             cases reducing to plain integer matrix products, a hand-worked
+             example in tests/golden/forward_example.txt
+  packer  -- Eckart-Young-Mirsky tail energy, brute force over random and
+             grid rank-r candidates, the eigenvector route, the p = 1/2
+             identity with eq 1, the isotropic (C = I) reduction
+"""

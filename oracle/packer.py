@@ -1,0 +1,109 @@
+"""Construction of a packed ARCHead head on small inputs (the tiny config).
+
+The paper's construction algorithm (section 3.4, Algorithm 1) is cut off in
+the extracted text right after its inputs (W, H, r_c, r_r, g, p, lambda).
+This module takes the plainest reading of equations 2-5 and the INT8 text
+after eq 7, in the paper's order and notation:
+
+1. damped metric (section 3.1, eq 2): C = H^T H / N, c_bar = mean(diag C),
+   C_lambda = C + lambda c_bar I = Q Lambda Q^T,
+   T_p = Q Lambda^p Q^T, T_p^-1 = Q Lambda^-p Q^T;
+2. rank-r_c core A_c B_c (section 3.2, text under eq 3): a truncated SVD of W
+   in the plain Frobenius sense, sqrt(Sigma) to each side;
+3. eq 3: Q5 on A_c (row scales), Q8 on B_c (row scales), SC4 = signed INT4
+   with fp16 (row, g-group) scales on W - A_c B_c (the unquantised core, as
+   eq 3 writes it); W_d = Q5(A_c) Q8(B_c) + Q_SC4(W - A_c B_c);
+4. E = W - W_d (text under eq 3);
+5. eqs 4-5: truncated SVD of E T_p to rank r_r, A_w = U Sigma,
+   B_w = V^T T_p^-1.  The paper uses a randomised SVD; the oracle takes the
+   exact one, which is the object the conditional-optimality statement
+   (eqs 8-9) is about;
+6. INT8 correction factors (text after eq 7): A_w row-wise, B_w group-wise
+   with group g along d.
+
+It returns the packed fields in the canonical host layout plus every
+intermediate, so the tests can check eqs 1, 8 and 9 on them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layout import pack_r4
+from .quant import dequantize_groups, quantize_groups
+
+
+def metric_transform(H: np.ndarray, p: float, lam: float) -> dict:
+    """Eq 2: damped activation covariance and its p-th power (and inverse)."""
+    H = np.asarray(H, dtype=np.float64)
+    N, D = H.shape
+    C = H.T @ H / N
+    c_bar = float(np.mean(np.diag(C)))
+    C_lam = C + lam * c_bar * np.eye(D)
+    evals, Q = np.linalg.eigh(C_lam)
+    if evals.min() <= 0:
+        raise ValueError("damped covariance is not positive definite; raise lambda")
+    T = (Q * evals ** p) @ Q.T
+    T_inv = (Q * evals ** (-p)) @ Q.T
+    return {"C": C, "c_bar": c_bar, "C_lam": C_lam, "Q": Q, "evals": evals,
+            "T": T, "T_inv": T_inv, "p": p, "lam": lam}
+
+
+def logit_error(H: np.ndarray, Delta: np.ndarray) -> float:
+    """Eq 1: (1/N) ||H Delta^T||_F^2."""
+    N = H.shape[0]
+    return float(np.sum(np.square(H @ Delta.T)) / N)
+
+
+def metric_objective(E: np.ndarray, A: np.ndarray, B: np.ndarray, T: np.ndarray) -> float:
+    """Eq 8: ||(E - A B) T_p||_F^2."""
+    return float(np.sum(np.square((E - A @ B) @ T)))
+
+
+def truncated_svd(M: np.ndarray, rank: int):
+    U, S, Vt = np.linalg.svd(M, full_matrices=False)
+    return U[:, :rank], S[:rank], Vt[:rank], S
+
+
+def correction(E: np.ndarray, T: np.ndarray, T_inv: np.ndarray, r: int) -> dict:
+    """Eqs 4-5: A_w = U_r Sigma_r, B_w = V_r^T T_p^-1 from the SVD of E T_p."""
+    E_t = E @ T
+    U, S, Vt, S_all = truncated_svd(E_t, r)
+    return {"E_tilde": E_t, "A_w": U * S[None, :], "B_w": Vt @ T_inv,
+            "sigma": S_all}
+
+
+def pack(W: np.ndarray, H: np.ndarray, k: int, r: int, g: int,
+         p: float = 0.75, lam: float = 1e-2) -> tuple[dict, dict]:
+    """Build the packed fields of W (V x d) from calibration states H (N x d)."""
+    W = np.asarray(W, dtype=np.float64)
+    V, d = W.shape
+    met = metric_transform(H, p, lam)
+
+    # rank-k core, sqrt of the singular values to each side
+    U, S, Vt, _ = truncated_svd(W, k)
+    A_c = U * np.sqrt(S)[None, :]
+    B_c = np.sqrt(S)[:, None] * Vt
+
+    # eq 3
+    A5, sA = quantize_groups(A_c, 5, None)
+    B8, sB = quantize_groups(B_c, 8, None)
+    R4v, sR = quantize_groups(W - A_c @ B_c, 4, g)
+    W_d = (dequantize_groups(A5, sA, None) @ dequantize_groups(B8, sB, None)
+           + dequantize_groups(R4v, sR, g))
+    E = W - W_d
+
+    # eqs 4-5
+    corr = correction(E, met["T"], met["T_inv"], r)
+    A_w, B_w = corr["A_w"], corr["B_w"]
+
+    # INT8 correction factors: A_w row-wise, B_w group-wise
+    C8, sC = quantize_groups(A_w, 8, None)
+    D8, sD = quantize_groups(B_w, 8, g)
+
+    fields = {"V": V, "d": d, "k": k, "r": r, "g": g,
+              "A5": A5, "sA": sA, "B8": B8, "sB": sB,
+              "R4": pack_r4(R4v), "sR": sR,
+              "C8": C8, "sC": sC, "D8": D8, "sD": sD}
+    inter = {"metric": met, "A_c": A_c, "B_c": B_c, "R4_values": R4v,
+             "W_d": W_d, "E": E, **corr}
+    return fields, inter
