@@ -1,0 +1,210 @@
+"""Benchmark of the packed ARCHead LM-head forward on one MI355X.
+
+One step = one full forward of the packed head (projection, vocabulary-tile
+kernel, top-1 reduction) over one batch of M synthetic bf16 hidden states,
+with the packed fields already resident in HBM.  The headline workload is the
+Qwen3-8B-shaped head (V=151936, d=4096, k=256, r=64, g=128) at M=1 (decode).
+Three independent copies of the packed head are rotated so that no step finds
+the previous step's 357 MB in the 256 MB last-level cache.
+
+Prints ONE JSON line.  Besides the headline numbers it carries:
+  roofline      the vocabulary-tile kernel against HBM bandwidth; its time is
+                taken with HIP events recorded by the library on the same
+                stream immediately around that kernel;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample;
+  secondary     the same measurement at M=2048 (prefill, MFMA-bound) and the
+                other workloads, with fewer steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA
+METRIC = "packed-head tokens/s + HBM GB/s (M=1) and MFMA% (M=2048), 151936x4096 head"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def vtile_bytes(V, d, k, r, g, M):
+    """Algorithmic HBM bytes of one vocabulary-tile launch: every packed field
+    it reads once (R4 4 bits, sR fp16 per group, A5 5 bits, sA, C8 8 bits, sC),
+    X read once, logits written once."""
+    per_row = d // 2 + 2 * (d // g) + (5 * k + 7) // 8 + 2 + r + 2
+    return V * per_row + M * d * 2 + M * V * 4
+
+
+def path_flops(V, d, k, r, M):
+    """Algorithmic flops of the whole factored forward (eq 7): 2 M (Vd + Vk + Vr + kd + rd)."""
+    return 2 * M * (V * d + V * k + V * r + k * d + r * d)
+
+
+def read_traffic(kernel_tag, workload):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    one exists for this kernel and workload (profiles/<kernel>_<workload>_counters.json)."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        data = json.load(fh)
+    return data.get("hbm_bytes_per_launch")
+
+
+def measure(name, steps, warmup, copies, path="auto", with_logits=True):
+    import torch
+    from packed_quantized_lm_amd import PackedHead, x_tensor_from_bits
+    from packed_quantized_lm_amd.synth import make_config
+
+    t0 = time.time()
+    c = make_config(name)
+    V, d, k, r, g, M = (c[n] for n in ("V", "d", "k", "r", "g", "M"))
+    heads = [PackedHead(c) for _ in range(copies)]
+    for h in heads:
+        h.reserve(M)
+    packed = heads[0].packed_bytes()
+    log(f"{name}: generated + loaded {copies} copies in {time.time() - t0:.1f}s")
+    X = x_tensor_from_bits(c["X"])
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda") if with_logits else None
+    arg = torch.empty((M,), dtype=torch.int32, device="cuda")
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    eva = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in evb + eva:      # torch creates the HIP event on its first record
+        ev.record()
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        heads[i % copies].forward_into(X, logits, arg, path=path)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        heads[i % copies].forward_timed(X, logits, arg, evb[i], eva[i], path=path)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    kern_ms = np.array([evb[i].elapsed_time(eva[i]) for i in range(steps)])
+    del heads
+    torch.cuda.synchronize()
+    step_s = total_ms / 1e3 / steps
+    kern_s = float(np.mean(kern_ms)) / 1e3
+    vb = vtile_bytes(V, d, k, r, g, M)
+    fl = path_flops(V, d, k, r, M)
+    return {
+        "workload": name, "V": V, "d": d, "k": k, "r": r, "g": g, "M": M,
+        "ms_per_step": total_ms / steps, "tokens_per_s": M / step_s,
+        "vtile_us_mean": kern_s * 1e6, "vtile_us_p10": float(np.percentile(kern_ms, 10)) * 1e3,
+        "vtile_us_p90": float(np.percentile(kern_ms, 90)) * 1e3,
+        "packed_bytes": packed, "vtile_bytes": vb,
+        "vtile_GBs": vb / kern_s / 1e9, "step_GBs_over_packed": packed / step_s / 1e9,
+        "path_TFLOPs": fl / step_s / 1e12, "steps": steps,
+    }
+
+
+def cpu_baseline(name="qwen_m1", budget_s=15.0):
+    """The oracle as it stands (oracle/forward.py, fp64, numpy BLAS) on a
+    bounded sample of vocabulary rows of the workload, scaled to tokens/s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import forward
+    from packed_quantized_lm_amd.synth import make_config
+
+    c = make_config(name)
+    V, M = c["V"], c["M"]
+    block = 8192
+    done, t = 0, 0.0
+    while done < V and t < budget_s:
+        rows = np.arange(done, min(V, done + block))
+        t0 = time.perf_counter()
+        forward.forward(c, c["X"], rows=rows)
+        t += time.perf_counter() - t0
+        done += rows.size
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    full_s = t * V / done
+    return {"value": M / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{name}: oracle fp64 forward over vocabulary rows 0..{done - 1} of {V} "
+                      f"({t:.1f} s), scaled to the full head"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--workload", default="qwen_m1")
+    ap.add_argument("--path", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the packed head's "
+              "forward is measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from packed_quantized_lm_amd import load_library
+    load_library()
+
+    head = measure(args.workload, args.steps, args.warmup, args.copies, path=args.path)
+    log(json.dumps(head))
+    secondary = []
+    if not args.no_secondary:
+        for name, steps in [("qwen_m2048", max(5, args.steps // 20)), ("qwen_m32", args.steps),
+                            ("large_m8", args.steps)]:
+            if name == args.workload:
+                continue
+            s = measure(name, steps, max(2, args.warmup // 4), args.copies, path=args.path)
+            s["mfma_frac"] = s["path_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+            s["hbm_frac"] = s["vtile_GBs"] / HBM_PEAK_GBS
+            log(json.dumps(s))
+            secondary.append(s)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload)
+        log(json.dumps(cpu))
+
+    traffic = read_traffic("vtile", args.workload)
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: V={head['V']} d={head['d']} k={head['k']} "
+                               f"r={head['r']} g={head['g']} M={head['M']}, 3 rotated copies",
+                   "packed_bytes": head["packed_bytes"],
+                   "step_GBs_over_packed": head["step_GBs_over_packed"]},
+        "roofline": {"bound": "hbm", "achieved": head["vtile_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["vtile_GBs"] / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "vtile (a2)", "kernel_us": head["vtile_us_mean"],
+                     "bytes_per_launch": head["vtile_bytes"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * archead.h -- C ABI of the packed ARCHead LM-head forward for MI355X (gfx950).
+ *
+ * The operation (ARCHead paper, "Activation-Metric Residual Correction for
+ * LLM Output Heads", section 3.2):
+ *   eq 3  W_d   = Q5(A_c) Q8(B_c) + Q_SC4(W - A_c B_c)
+ *   eq 6  W_hat = W_d + A_w B_w                (A_w, B_w stored as row/group
+ *                                               INT8, text after eq 7)
+ *   eq 7  logits = X W_d^T + (X B_w^T) A_w^T   (factored: no dense W_hat)
+ * In the stored fields (section 3.3, state-dict accounting paragraph):
+ *   W_hat[v,j] = sA[v] sum_i A5[v,i] sB[i] B8[i,j]
+ *              + sR[v, j/g] R4[v,j]
+ *              + sC[v] sum_i C8[v,i] sD[i, j/g] D8[i,j]
+ *   logits[m,v] = sum_j X[m,j] W_hat[v,j]
+ * Notation follows the paper's statement of the problem (section 3.4
+ * inputs): vocabulary V, hidden size d (the paper's D), core rank k (r_c),
+ * correction rank r (r_r), group size g, and M hidden states.
+ *
+ * Canonical HOST layout of the packed fields (all row-major):
+ *   A5  int8     V x k      values in [-16, 15] (5-bit core factor)
+ *   sA  uint16   V          fp16 bit patterns, one scale per row
+ *   B8  int8     k x d      8-bit core factor
+ *   sB  uint16   k          fp16, one scale per row
+ *   R4  uint8    V x d/2    SC4 residual: byte [v,c] = column 2c in the low
+ *                           nibble, column 2c+1 in the high nibble, 4-bit
+ *                           two's complement
+ *   sR  uint16   V x d/g    fp16, one scale per (row, g-column group)
+ *   C8  int8     V x r      quantised A_w (row-wise INT8)
+ *   sC  uint16   V          fp16, one scale per row
+ *   D8  int8     r x d      quantised B_w (group-wise INT8)
+ *   sD  uint16   r x d/g    fp16, one scale per (row, g-column group)
+ * The library re-lays these out into its own device layout at load time
+ * (A5 at 5 bits per value) and never keeps a dense W_hat anywhere.
+ *
+ * Streams: every call that touches the device takes a hipStream_t (as void*;
+ * NULL = the null stream).  Kernels are enqueued on that stream; the library
+ * never synchronises it on the forward path and never allocates there once
+ * the workspace is large enough (see archead_reserve).
+ *
+ * Errors: every entry point returns an archead_status and never throws or
+ * aborts.  Arguments are validated before anything is enqueued.  A HIP
+ * failure maps to ARCHEAD_EHIP; archead_last_error() returns a thread-local
+ * text with the detail of the last failure on the calling thread.  NaN or
+ * Inf scales are not checked: they propagate into the logits.
+ */
+#ifndef ARCHEAD_H
+#define ARCHEAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARCHEAD_ABI_VERSION 1
+
+typedef struct archead_head *archead_t;
+
+typedef enum archead_status {
+    ARCHEAD_OK = 0,
+    ARCHEAD_EINVAL = 1, /* NULL pointer, bad handle, negative size, bad path */
+    ARCHEAD_ESHAPE = 2, /* shape the layout does not support (see pack_load) */
+    ARCHEAD_ERANGE = 3, /* a field value outside its integer range          */
+    ARCHEAD_ENOMEM = 4, /* device or host allocation failed                 */
+    ARCHEAD_EHIP = 5    /* a HIP runtime call failed                        */
+} archead_status;
+
+/* Kernel families for the vocabulary-tile step (archead_forward_path). */
+typedef enum archead_path {
+    ARCHEAD_PATH_AUTO = 0,   /* chosen from M                                  */
+    ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV with wave shuffles, small M     */
+    ARCHEAD_PATH_SKINNY = 2, /* register-dequantised MFMA, W streamed once     */
+    ARCHEAD_PATH_LDS = 3     /* LDS-staged fp16-dequantised MFMA, large M      */
+} archead_path;
+
+/*
+ * archead_pack_load -- build a device-resident packed head.
+ *
+ * Defines: the packed module of ARCHead paper section 3.3 (registers only
+ * the SC4 residual and its scales, the quantised core factors, the quantised
+ * correction factors and shape metadata; the dense V x D head is not kept).
+ *
+ * V, d, k, r, g  shape (see above).  Supported: V >= 1, V < 2^31;
+ *                d a multiple of 128; g a multiple of 32 dividing d;
+ *                0 <= k <= 4096, 0 <= r <= 4096 (k = 0 or r = 0 drop the
+ *                core or the correction term; the corresponding pointers
+ *                may then be NULL).  Otherwise ARCHEAD_ESHAPE.
+ * A5 .. sD       HOST pointers in the canonical layout above, borrowed for
+ *                the duration of the call only (the caller keeps ownership
+ *                and may free them on return).  NULL where required ->
+ *                ARCHEAD_EINVAL.  An A5 value outside [-16, 15] ->
+ *                ARCHEAD_ERANGE.
+ * hip_stream     stream used for the host-to-device copies; the call waits
+ *                for them before returning.
+ * out            receives the handle; set to NULL on failure.  The handle
+ *                owns all device memory it allocates (packed fields in the
+ *                device layout plus a workspace) until archead_free.
+ */
+archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int64_t g,
+                                 const int8_t *A5, const uint16_t *sA,
+                                 const int8_t *B8, const uint16_t *sB,
+                                 const uint8_t *R4, const uint16_t *sR,
+                                 const int8_t *C8, const uint16_t *sC,
+                                 const int8_t *D8, const uint16_t *sD,
+                                 void *hip_stream, archead_t *out);
+
+/*
+ * archead_reserve -- size the handle's device workspace for up to M_max
+ * hidden states per call, so that later forward calls with M <= M_max never
+ * allocate.  A forward call with a larger M grows the workspace itself
+ * (hipMalloc; the old buffer is freed after the device has drained it).
+ * M_max < 0 -> ARCHEAD_EINVAL; M_max > 2^20 -> ARCHEAD_ESHAPE.
+ */
+archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream);
+
+/*
+ * archead_forward -- logits = X W_hat^T, factored as in eq 7 (ARCHead paper
+ * section 3.2; "the inference computation is factored, avoiding the
+ * reconstruction of a dense matrix").
+ *
+ * M        number of hidden states, 0 <= M <= 2^20 (M = 0 is a no-op that
+ *          succeeds whatever X and logits are).
+ * X        DEVICE pointer, bf16, M x d row-major, 16-byte aligned.
+ * logits   DEVICE pointer, fp32, M x V row-major, written in full.
+ * X and logits are caller-owned and must stay valid until the stream has
+ * passed this call.  Work is enqueued on hip_stream and not waited for.
+ * Numerics: integer fields are used exactly; accumulation is fp32; the
+ * large-M path rounds the product sR*R4 once to fp16 (see archead_path).
+ */
+archead_status archead_forward(archead_t h, int64_t M, const void *X, float *logits,
+                               void *hip_stream);
+
+/*
+ * archead_forward_argmax -- as archead_forward, plus the per-token top-1
+ * index: argmax[m] = min{ v : logits[m,v] = max_u logits[m,u] } (the top-1
+ * token whose agreement with the dense head the ARCHead pages report).
+ *
+ * logits   DEVICE fp32 M x V, or NULL to skip writing the logits.
+ * argmax   DEVICE int32 M, written in full.  NaN logits make the index of
+ *          that row unspecified (but within [0, V)).
+ */
+archead_status archead_forward_argmax(archead_t h, int64_t M, const void *X, float *logits,
+                                      int32_t *argmax, void *hip_stream);
+
+/*
+ * archead_forward_path -- archead_forward_argmax with the vocabulary-tile
+ * kernel family forced (archead_path).  logits and argmax may each be NULL
+ * (not both).  An unknown path -> ARCHEAD_EINVAL.  Every path computes the
+ * same function to within the documented rounding.
+ */
+archead_status archead_forward_path(archead_t h, int64_t M, const void *X, float *logits,
+                                     int32_t *argmax, int path, void *hip_stream);
+
+/*
+ * archead_forward_timed -- archead_forward_path that also records two HIP
+ * events on hip_stream immediately before and after the vocabulary-tile
+ * kernel (the step that streams the packed fields), so that a caller can
+ * time that kernel alone.  ev_before / ev_after are hipEvent_t values (as
+ * void*) created by the caller on the current device; NULL -> ARCHEAD_EINVAL.
+ * For benchmarking and profiling; the results are those of
+ * archead_forward_path.
+ */
+archead_status archead_forward_timed(archead_t h, int64_t M, const void *X, float *logits,
+                                     int32_t *argmax, int path, void *hip_stream,
+                                     void *ev_before, void *ev_after);
+
+/*
+ * archead_packed_bytes -- eq 10 of the ARCHead paper: the sum over the
+ * registered packed buffers of numel x element size (A5 counted at 5 bits,
+ * R4 at 4 bits, int8 fields at 8, scales at 16; each buffer rounded up to a
+ * byte).  Device padding and the workspace are excluded.
+ */
+archead_status archead_packed_bytes(archead_t h, uint64_t *bytes);
+
+/* archead_device_bytes -- device memory the handle holds right now
+ * (packed fields with their tile padding, plus the workspace). */
+archead_status archead_device_bytes(archead_t h, uint64_t *bytes);
+
+/* archead_free -- release the handle and all its device memory (waits for the
+ * device first).  NULL is accepted (no-op).  Using h afterwards is an error
+ * the library detects while the memory has not been reused (ARCHEAD_EINVAL). */
+archead_status archead_free(archead_t h);
+
+/* Static text for a status code. */
+const char *archead_status_string(archead_status s);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *archead_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARCHEAD_H */

@@ -1,0 +1,179 @@
+"""Thin Python binding of libarchead.so (the C ABI in include/archead.h).
+
+Argument marshalling only: numpy arrays in the canonical host layout go to
+archead_pack_load; torch CUDA tensors provide device memory for X, logits and
+argmax, and torch's current stream is passed down as the hipStream_t.  Every
+step of the forward runs in the library's HIP kernels.  There is no other
+implementation behind this module: if the library is missing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libarchead.so")
+
+OK, EINVAL, ESHAPE, ERANGE, ENOMEM, EHIP = range(6)
+PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_LDS = range(4)
+PATHS = {"auto": PATH_AUTO, "gemv": PATH_GEMV, "skinny": PATH_SKINNY, "lds": PATH_LDS}
+
+# exported symbol -> (restype, argtypes)
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "archead_pack_load": (ctypes.c_int, [_I64] * 5 + [_VP] * 10 + [_VP, ctypes.POINTER(_VP)]),
+    "archead_reserve": (ctypes.c_int, [_VP, _I64, _VP]),
+    "archead_forward": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP]),
+    "archead_forward_argmax": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP]),
+    "archead_forward_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP]),
+    "archead_forward_timed": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP]),
+    "archead_packed_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
+    "archead_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
+    "archead_free": (ctypes.c_int, [_VP]),
+    "archead_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "archead_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class ArcheadError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libarchead.so (built by packed_quantized_lm_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m packed_quantized_lm_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        lib = load_library()
+        detail = lib.archead_last_error().decode() or lib.archead_status_string(status).decode()
+        raise ArcheadError(status, where, detail)
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_FIELD_DTYPES = [("A5", np.int8), ("sA", np.uint16), ("B8", np.int8), ("sB", np.uint16),
+                 ("R4", np.uint8), ("sR", np.uint16), ("C8", np.int8), ("sC", np.uint16),
+                 ("D8", np.int8), ("sD", np.uint16)]
+
+
+class PackedHead:
+    """A packed ARCHead head resident on the current HIP device."""
+
+    def __init__(self, fields: dict, stream=None):
+        lib = load_library()
+        self.V, self.d, self.k, self.r, self.g = (int(fields[n]) for n in ("V", "d", "k", "r", "g"))
+        arrs = {}
+        for name, dt in _FIELD_DTYPES:
+            a = fields.get(name)
+            arrs[name] = None if a is None else np.ascontiguousarray(a, dtype=dt)
+        handle = ctypes.c_void_p()
+        st = lib.archead_pack_load(self.V, self.d, self.k, self.r, self.g,
+                                   *[_np_ptr(arrs[n]) for n, _ in _FIELD_DTYPES],
+                                   _stream_handle(stream), ctypes.byref(handle))
+        _check(st, "archead_pack_load")
+        self._h = handle
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("head was freed")
+        return self._h
+
+    def reserve(self, M_max: int, stream=None):
+        _check(load_library().archead_reserve(self.handle, int(M_max), _stream_handle(stream)),
+               "archead_reserve")
+
+    def packed_bytes(self) -> int:
+        out = ctypes.c_uint64()
+        _check(load_library().archead_packed_bytes(self.handle, ctypes.byref(out)), "archead_packed_bytes")
+        return out.value
+
+    def device_bytes(self) -> int:
+        out = ctypes.c_uint64()
+        _check(load_library().archead_device_bytes(self.handle, ctypes.byref(out)), "archead_device_bytes")
+        return out.value
+
+    def forward_into(self, X, logits, argmax, path: str | int = "auto", stream=None):
+        """Enqueue the forward writing into preallocated torch tensors (either
+        of logits / argmax may be None).  X: bf16 (or int16 bit patterns) M x d."""
+        p = PATHS[path] if isinstance(path, str) else int(path)
+        M = int(X.shape[0])
+        st = load_library().archead_forward_path(
+            self.handle, M, ctypes.c_void_p(X.data_ptr()),
+            None if logits is None else ctypes.c_void_p(logits.data_ptr()),
+            None if argmax is None else ctypes.c_void_p(argmax.data_ptr()),
+            p, _stream_handle(stream))
+        _check(st, "archead_forward_path")
+
+    def forward_timed(self, X, logits, argmax, ev_before, ev_after, path: str | int = "auto",
+                      stream=None):
+        """forward_into that also records the torch.cuda.Event pair around the
+        vocabulary-tile kernel on the same stream."""
+        p = PATHS[path] if isinstance(path, str) else int(path)
+        st = load_library().archead_forward_timed(
+            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()),
+            None if logits is None else ctypes.c_void_p(logits.data_ptr()),
+            None if argmax is None else ctypes.c_void_p(argmax.data_ptr()),
+            p, _stream_handle(stream), ctypes.c_void_p(ev_before.cuda_event),
+            ctypes.c_void_p(ev_after.cuda_event))
+        _check(st, "archead_forward_timed")
+
+    def forward(self, X, want_logits: bool = True, want_argmax: bool = False,
+                path: str | int = "auto", stream=None):
+        """Returns (logits fp32 M x V or None, argmax int32 M or None) as torch tensors."""
+        import torch
+        if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("X must hold bf16 values")
+        if X.dim() != 2 or X.shape[1] != self.d or not X.is_contiguous():
+            raise ValueError(f"X must be a contiguous M x {self.d} tensor")
+        M = X.shape[0]
+        logits = torch.empty((M, self.V), dtype=torch.float32, device=X.device) if want_logits else None
+        argmax = torch.empty((M,), dtype=torch.int32, device=X.device) if want_argmax else None
+        self.forward_into(X, logits, argmax, path=path, stream=stream)
+        return logits, argmax
+
+    def close(self):
+        if self._h is not None:
+            _check(load_library().archead_free(self._h), "archead_free")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def x_tensor_from_bits(bits: np.ndarray, device="cuda"):
+    """bf16 bit patterns (uint16 numpy) -> torch.bfloat16 device tensor (bitwise)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to(device).view(torch.bfloat16)

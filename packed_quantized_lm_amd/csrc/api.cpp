@@ -1,0 +1,429 @@
+// api.cpp -- the C ABI declared in include/archead.h.
+//
+// Host side only: argument validation, the one-time relayout and upload of
+// the packed fields (pack_load), the per-handle workspace, and dispatch of the
+// forward kernels on the caller's stream.
+#include "archead.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+
+using namespace archead;
+
+namespace {
+
+constexpr uint64_t kMagic = 0x41524348454144ull; // "ARCHEAD"
+constexpr int64_t kMaxM = int64_t(1) << 20;
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_err;
+
+std::mutex g_live_mu;
+std::set<const void *> g_live;
+
+archead_status fail(archead_status s, const std::string &msg)
+{
+    g_err = msg;
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                          \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail(ARCHEAD_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));      \
+    } while (0)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+} // namespace
+
+struct archead_head {
+    uint64_t magic;
+    Shape s;
+    DevHead dev;
+    void *block;        // one allocation holding every packed array
+    size_t block_bytes;
+    void *ws;           // workspace
+    size_t ws_bytes;
+    int64_t ws_M;       // largest M the workspace holds
+    int device;
+};
+
+namespace {
+
+bool live(archead_t h)
+{
+    std::lock_guard<std::mutex> g(g_live_mu);
+    return h && g_live.count(h) && h->magic == kMagic;
+}
+
+struct WsLayout {
+    size_t t16, s16, xsneg, part, total;
+};
+
+int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
+
+int64_t max_n_part(const Shape &s)
+{
+    DevHead tmp{};
+    tmp.s = s;
+    return std::max<int64_t>(skinny_n_part(tmp, 1), 1);
+}
+
+WsLayout ws_layout(const Shape &s, int64_t Mmax)
+{
+    const int64_t Mp = round_m(std::max<int64_t>(Mmax, 1));
+    WsLayout L;
+    size_t off = 0;
+    L.t16 = off;
+    off = align_up(off + size_t(2) * Mp * s.kpad() * 2);
+    L.s16 = off;
+    off = align_up(off + size_t(2) * Mp * s.rpad() * 2);
+    L.xsneg = off;
+    off = align_up(off + size_t(s.G()) * Mp * 4);
+    L.part = off;
+    off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
+    L.total = off;
+    return L;
+}
+
+archead_status grow_workspace(archead_t h, int64_t M, hipStream_t st)
+{
+    if (M <= h->ws_M && h->ws)
+        return ARCHEAD_OK;
+    WsLayout L = ws_layout(h->s, M);
+    if (h->ws) {
+        HIP_TRY(hipDeviceSynchronize());
+        HIP_TRY(hipFree(h->ws));
+        h->ws = nullptr;
+        h->ws_bytes = 0;
+        h->ws_M = 0;
+    }
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, L.total);
+    if (e != hipSuccess)
+        return fail(ARCHEAD_ENOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
+    HIP_TRY(hipMemsetAsync(p, 0, L.total, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    h->ws = p;
+    h->ws_bytes = L.total;
+    h->ws_M = M;
+    return ARCHEAD_OK;
+}
+
+Work make_work(archead_t h, int64_t M)
+{
+    WsLayout L = ws_layout(h->s, h->ws_M);
+    char *b = (char *)h->ws;
+    Work w;
+    w.M = M;
+    w.Mp = round_m(h->ws_M);
+    w.t16 = (uint16_t *)(b + L.t16);
+    w.s16 = (uint16_t *)(b + L.s16);
+    w.xsneg = (float *)(b + L.xsneg);
+    w.part = (uint64_t *)(b + L.part);
+    w.n_part = 0;
+    return w;
+}
+
+archead_status validate_shape(int64_t V, int64_t d, int64_t k, int64_t r, int64_t g)
+{
+    if (V < 1 || V >= (int64_t(1) << 31))
+        return fail(ARCHEAD_ESHAPE, "V must satisfy 1 <= V < 2^31");
+    if (d < kKChunk || d % kKChunk)
+        return fail(ARCHEAD_ESHAPE, "d must be a positive multiple of 128");
+    if (g < kKStep || g % kKStep || d % g)
+        return fail(ARCHEAD_ESHAPE, "g must be a multiple of 32 that divides d");
+    if (k < 0 || k > 4096 || r < 0 || r > 4096)
+        return fail(ARCHEAD_ESHAPE, "k and r must lie in [0, 4096]");
+    if ((V + kVB - 1) / kVB * (d / 2) * kVB > (int64_t(1) << 40))
+        return fail(ARCHEAD_ESHAPE, "head too large");
+    return ARCHEAD_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *archead_status_string(archead_status s)
+{
+    switch (s) {
+    case ARCHEAD_OK: return "ARCHEAD_OK";
+    case ARCHEAD_EINVAL: return "ARCHEAD_EINVAL: invalid argument";
+    case ARCHEAD_ESHAPE: return "ARCHEAD_ESHAPE: unsupported shape";
+    case ARCHEAD_ERANGE: return "ARCHEAD_ERANGE: field value out of range";
+    case ARCHEAD_ENOMEM: return "ARCHEAD_ENOMEM: allocation failed";
+    case ARCHEAD_EHIP: return "ARCHEAD_EHIP: HIP runtime error";
+    }
+    return "ARCHEAD: unknown status";
+}
+
+const char *archead_last_error(void) { return g_err.c_str(); }
+
+archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int64_t g,
+                                 const int8_t *A5, const uint16_t *sA, const int8_t *B8,
+                                 const uint16_t *sB, const uint8_t *R4, const uint16_t *sR,
+                                 const int8_t *C8, const uint16_t *sC, const int8_t *D8,
+                                 const uint16_t *sD, void *hip_stream, archead_t *out)
+{
+    g_err.clear();
+    if (!out)
+        return fail(ARCHEAD_EINVAL, "out is NULL");
+    *out = nullptr;
+    archead_status st = validate_shape(V, d, k, r, g);
+    if (st != ARCHEAD_OK)
+        return st;
+    if (!R4 || !sR)
+        return fail(ARCHEAD_EINVAL, "R4 and sR are required");
+    if (k > 0 && (!A5 || !sA || !B8 || !sB))
+        return fail(ARCHEAD_EINVAL, "A5, sA, B8, sB are required when k > 0");
+    if (r > 0 && (!C8 || !sC || !D8 || !sD))
+        return fail(ARCHEAD_EINVAL, "C8, sC, D8, sD are required when r > 0");
+    for (int64_t i = 0; i < V * k; ++i)
+        if (A5[i] < -16 || A5[i] > 15)
+            return fail(ARCHEAD_ERANGE, "A5 value outside [-16, 15] at flat index " + std::to_string(i));
+
+    Shape s{V, d, k, r, g};
+    // device block layout
+    size_t off = 0;
+    auto place = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1));
+        return o;
+    };
+    const size_t o_r4 = place(s.n_r4() * 4), o_sr = place(s.n_sr() * 2);
+    const size_t o_a5n = place(s.n_a5n() * 4), o_a5h = place(s.n_a5h() * 4);
+    const size_t o_c8 = place(s.n_c8() * 4), o_sa = place(s.n_rows() * 2);
+    const size_t o_sc = place(s.n_rows() * 2), o_b8 = place(size_t(k) * d);
+    const size_t o_sb = place(size_t(k) * 4), o_d8 = place(size_t(r) * d);
+    const size_t o_sd = place(size_t(r) * s.G() * 4);
+    const size_t total = off;
+
+    std::vector<char> host;
+    try {
+        host.assign(total, 0);
+    } catch (...) {
+        return fail(ARCHEAD_ENOMEM, "host staging allocation failed");
+    }
+    char *hb = host.data();
+    HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_a5n),
+                     (uint32_t *)(hb + o_a5h), (uint32_t *)(hb + o_c8), (uint16_t *)(hb + o_sa),
+                     (uint16_t *)(hb + o_sc), (float *)(hb + o_sb), (float *)(hb + o_sd)};
+    relayout(s, A5, sA, sB, R4, sR, C8, sC, sD, img,
+             (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency())));
+    if (k > 0)
+        std::memcpy(hb + o_b8, B8, size_t(k) * d);
+    if (r > 0)
+        std::memcpy(hb + o_d8, D8, size_t(r) * d);
+
+    hipStream_t stream = (hipStream_t)hip_stream;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    void *block = nullptr;
+    hipError_t e = hipMalloc(&block, total);
+    if (e != hipSuccess)
+        return fail(ARCHEAD_ENOMEM, std::string("hipMalloc of the packed head: ") + hipGetErrorString(e));
+    e = hipMemcpyAsync(block, hb, total, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        (void)hipFree(block);
+        return fail(ARCHEAD_EHIP, std::string("upload of the packed head: ") + hipGetErrorString(e));
+    }
+
+    archead_head *h = new (std::nothrow) archead_head();
+    if (!h) {
+        (void)hipFree(block);
+        return fail(ARCHEAD_ENOMEM, "handle allocation failed");
+    }
+    char *db = (char *)block;
+    h->magic = kMagic;
+    h->s = s;
+    h->dev.s = s;
+    h->dev.r4 = (const uint32_t *)(db + o_r4);
+    h->dev.sr = (const uint16_t *)(db + o_sr);
+    h->dev.a5n = (const uint32_t *)(db + o_a5n);
+    h->dev.a5h = (const uint32_t *)(db + o_a5h);
+    h->dev.c8 = (const uint32_t *)(db + o_c8);
+    h->dev.sa = (const uint16_t *)(db + o_sa);
+    h->dev.sc = (const uint16_t *)(db + o_sc);
+    h->dev.b8 = (const int8_t *)(db + o_b8);
+    h->dev.sb = (const float *)(db + o_sb);
+    h->dev.d8 = (const int8_t *)(db + o_d8);
+    h->dev.sd = (const float *)(db + o_sd);
+    h->block = block;
+    h->block_bytes = total;
+    h->ws = nullptr;
+    h->ws_bytes = 0;
+    h->ws_M = 0;
+    h->device = dev;
+    st = grow_workspace(h, 1, stream);
+    if (st != ARCHEAD_OK) {
+        (void)hipFree(block);
+        delete h;
+        return st;
+    }
+    {
+        std::lock_guard<std::mutex> gl(g_live_mu);
+        g_live.insert(h);
+    }
+    *out = h;
+    return ARCHEAD_OK;
+}
+
+archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream)
+{
+    g_err.clear();
+    if (!live(h))
+        return fail(ARCHEAD_EINVAL, "invalid or freed handle");
+    if (M_max < 0)
+        return fail(ARCHEAD_EINVAL, "M_max < 0");
+    if (M_max > kMaxM)
+        return fail(ARCHEAD_ESHAPE, "M_max above 2^20");
+    HIP_TRY(hipSetDevice(h->device));
+    return grow_workspace(h, std::max<int64_t>(M_max, 1), (hipStream_t)hip_stream);
+}
+
+static archead_status forward_impl(archead_t h, int64_t M, const void *X, float *logits,
+                                   int32_t *argmax, int path, void *hip_stream, hipEvent_t ev0,
+                                   hipEvent_t ev1)
+{
+    g_err.clear();
+    if (!live(h))
+        return fail(ARCHEAD_EINVAL, "invalid or freed handle");
+    if (M < 0)
+        return fail(ARCHEAD_EINVAL, "M < 0");
+    if (M > kMaxM)
+        return fail(ARCHEAD_ESHAPE, "M above 2^20");
+    if (path < ARCHEAD_PATH_AUTO || path > ARCHEAD_PATH_LDS)
+        return fail(ARCHEAD_EINVAL, "unknown path");
+    if (M == 0)
+        return ARCHEAD_OK;
+    if (!logits && !argmax)
+        return fail(ARCHEAD_EINVAL, "logits and argmax are both NULL");
+    if (!X)
+        return fail(ARCHEAD_EINVAL, "X is NULL");
+    if (((uintptr_t)X) % 16)
+        return fail(ARCHEAD_EINVAL, "X must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)hip_stream;
+    HIP_TRY(hipSetDevice(h->device));
+    archead_status s = grow_workspace(h, M, st);
+    if (s != ARCHEAD_OK)
+        return s;
+
+    int chosen = path;
+    if (chosen == ARCHEAD_PATH_AUTO)
+        chosen = ARCHEAD_PATH_SKINNY;
+    if (chosen != ARCHEAD_PATH_SKINNY)
+        return fail(ARCHEAD_EINVAL, "path not available in this build");
+
+    Work w = make_work(h, M);
+    const uint16_t *Xb = (const uint16_t *)X;
+    HIP_TRY(launch_proj(h->dev, w, Xb, st));
+    int64_t n_part = 0;
+    if (ev0)
+        HIP_TRY(hipEventRecord(ev0, st));
+    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax != nullptr, st, &n_part));
+    if (ev1)
+        HIP_TRY(hipEventRecord(ev1, st));
+    if (argmax)
+        HIP_TRY(launch_argmax(w, n_part, argmax, st));
+    return ARCHEAD_OK;
+}
+
+archead_status archead_forward_path(archead_t h, int64_t M, const void *X, float *logits,
+                                    int32_t *argmax, int path, void *hip_stream)
+{
+    return forward_impl(h, M, X, logits, argmax, path, hip_stream, nullptr, nullptr);
+}
+
+archead_status archead_forward_timed(archead_t h, int64_t M, const void *X, float *logits,
+                                     int32_t *argmax, int path, void *hip_stream,
+                                     void *ev_before, void *ev_after)
+{
+    if (!ev_before || !ev_after) {
+        g_err = "ev_before and ev_after are required";
+        return ARCHEAD_EINVAL;
+    }
+    return forward_impl(h, M, X, logits, argmax, path, hip_stream, (hipEvent_t)ev_before,
+                        (hipEvent_t)ev_after);
+}
+
+archead_status archead_forward(archead_t h, int64_t M, const void *X, float *logits,
+                               void *hip_stream)
+{
+    if (!logits) {
+        g_err = "logits is NULL";
+        return ARCHEAD_EINVAL;
+    }
+    return archead_forward_path(h, M, X, logits, nullptr, ARCHEAD_PATH_AUTO, hip_stream);
+}
+
+archead_status archead_forward_argmax(archead_t h, int64_t M, const void *X, float *logits,
+                                      int32_t *argmax, void *hip_stream)
+{
+    if (!argmax) {
+        g_err = "argmax is NULL";
+        return ARCHEAD_EINVAL;
+    }
+    return archead_forward_path(h, M, X, logits, argmax, ARCHEAD_PATH_AUTO, hip_stream);
+}
+
+archead_status archead_packed_bytes(archead_t h, uint64_t *bytes)
+{
+    g_err.clear();
+    if (!live(h) || !bytes)
+        return fail(ARCHEAD_EINVAL, "invalid handle or NULL output");
+    const Shape &s = h->s;
+    auto B = [](uint64_t numel, uint64_t bits) { return (numel * bits + 7) / 8; };
+    const uint64_t G = s.G();
+    *bytes = B(s.V * s.d, 4) + B(s.V * G, 16) + B(s.V * s.k, 5) + B(s.V, 16) + B(s.k * s.d, 8) +
+             B(s.k, 16) + B(s.V * s.r, 8) + B(s.V, 16) + B(s.r * s.d, 8) + B(s.r * G, 16);
+    return ARCHEAD_OK;
+}
+
+archead_status archead_device_bytes(archead_t h, uint64_t *bytes)
+{
+    g_err.clear();
+    if (!live(h) || !bytes)
+        return fail(ARCHEAD_EINVAL, "invalid handle or NULL output");
+    *bytes = h->block_bytes + h->ws_bytes;
+    return ARCHEAD_OK;
+}
+
+archead_status archead_free(archead_t h)
+{
+    g_err.clear();
+    if (!h)
+        return ARCHEAD_OK;
+    {
+        std::lock_guard<std::mutex> gl(g_live_mu);
+        if (!g_live.count(h))
+            return fail(ARCHEAD_EINVAL, "invalid or already freed handle");
+        g_live.erase(h);
+    }
+    (void)hipSetDevice(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    if (h->ws)
+        (void)hipFree(h->ws);
+    if (h->block)
+        (void)hipFree(h->block);
+    h->magic = 0;
+    delete h;
+    if (e != hipSuccess)
+        return fail(ARCHEAD_EHIP, std::string("hipDeviceSynchronize: ") + hipGetErrorString(e));
+    return ARCHEAD_OK;
+}
+
+} // extern "C"

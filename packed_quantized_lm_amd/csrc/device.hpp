@@ -1,0 +1,147 @@
+// device.hpp -- gfx950 device helpers shared by the ARCHead kernels.
+//
+// Exact-integer dequantisation by exponent splicing: OR-ing an unsigned
+// integer u < 128 into the mantissa of bf16 128.0 (0x4300) gives the bf16
+// value 128 + u exactly (the ulp at 128 is 1).  Likewise fp16 1024.0
+// (0x6400) takes u < 1024 and gives 1024 + u.  Offset-binary storage
+// (u = q + bias) therefore turns into exact small integers with one mask-or
+// per column pair; the constant offset is removed inside the fp32 MFMA
+// accumulator (bf16 paths) or by one packed fp16 add (fp16 paths).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace archead {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr uint32_t kBf16Magic = 0x43004300u;  // bf16 pair (128, 128)
+constexpr uint32_t kF16Magic = 0x64006400u;   // fp16 pair (1024, 1024)
+constexpr float kR4Bias = 136.0f;             // 128 + 8: bf16 value of residual q is q + 136
+constexpr float kA5Bias = 144.0f;             // 128 + 16: bf16 value of core code a is a + 144
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+__device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n)
+{
+    return __builtin_amdgcn_alignbit(x, x, n);
+}
+
+// Residual dword (8 offset-binary nibbles, slot order of layout.hpp) ->
+// 8 bf16 values q + 136, columns in natural order.
+__device__ __forceinline__ u32x4 r4_bf16(uint32_t w)
+{
+    u32x4 o;
+    o.x = (w & 0x000F000Fu) | kBf16Magic;
+    o.y = ((w >> 4) & 0x000F000Fu) | kBf16Magic;
+    o.z = ((w >> 8) & 0x000F000Fu) | kBf16Magic;
+    o.w = ((w >> 12) & 0x000F000Fu) | kBf16Magic;
+    return o;
+}
+
+// Same nibbles -> 8 fp16 values q + 1032 (1024 + 8).
+__device__ __forceinline__ u32x4 r4_f16_biased(uint32_t w)
+{
+    u32x4 o;
+    o.x = (w & 0x000F000Fu) | kF16Magic;
+    o.y = ((w >> 4) & 0x000F000Fu) | kF16Magic;
+    o.z = ((w >> 8) & 0x000F000Fu) | kF16Magic;
+    o.w = ((w >> 12) & 0x000F000Fu) | kF16Magic;
+    return o;
+}
+
+// 5-bit core code of K-step q (0..3 within its high-bit dword): nibble plane
+// dword wn + high-bit dword wh -> 8 bf16 values a + 144.
+template <int Q>
+__device__ __forceinline__ u32x4 a5_bf16(uint32_t wn, uint32_t wh)
+{
+    u32x4 o;
+    o.x = ((wn & 0x000F000Fu) | kBf16Magic) | (rotr(wh, 4 * Q + 0) & 0x00100010u);
+    o.y = (((wn >> 4) & 0x000F000Fu) | kBf16Magic) | (rotr(wh, 4 * Q + 1) & 0x00100010u);
+    o.z = (((wn >> 8) & 0x000F000Fu) | kBf16Magic) | (rotr(wh, 4 * Q + 2) & 0x00100010u);
+    o.w = (((wn >> 12) & 0x000F000Fu) | kBf16Magic) | (rotr(wh, 4 * Q + 3) & 0x00100010u);
+    return o;
+}
+
+__device__ __forceinline__ u32x4 a5_bf16_q(uint32_t wn, uint32_t wh, int q)
+{
+    switch (q) {
+    case 0: return a5_bf16<0>(wn, wh);
+    case 1: return a5_bf16<1>(wn, wh);
+    case 2: return a5_bf16<2>(wn, wh);
+    default: return a5_bf16<3>(wn, wh);
+    }
+}
+
+// Exact fp32 -> bf16 pair for values that bf16 represents exactly (the low
+// 16 bits of both fp32 patterns are zero): take the two high halves.
+__device__ __forceinline__ uint32_t pack_hi_halves(float lo, float hi)
+{
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Correction factor bytes (offset binary c ^ 0x80, 8 columns in order) ->
+// 8 exact bf16 integers c.
+__device__ __forceinline__ u32x4 c8_bf16(u32x2 w)
+{
+    u32x4 o;
+    float f0 = (float)((w.x >> 0) & 0xFFu) - 128.0f;
+    float f1 = (float)((w.x >> 8) & 0xFFu) - 128.0f;
+    float f2 = (float)((w.x >> 16) & 0xFFu) - 128.0f;
+    float f3 = (float)((w.x >> 24) & 0xFFu) - 128.0f;
+    float f4 = (float)((w.y >> 0) & 0xFFu) - 128.0f;
+    float f5 = (float)((w.y >> 8) & 0xFFu) - 128.0f;
+    float f6 = (float)((w.y >> 16) & 0xFFu) - 128.0f;
+    float f7 = (float)((w.y >> 24) & 0xFFu) - 128.0f;
+    o.x = pack_hi_halves(f0, f1);
+    o.y = pack_hi_halves(f2, f3);
+    o.z = pack_hi_halves(f4, f5);
+    o.w = pack_hi_halves(f6, f7);
+    return o;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Order-preserving map of fp32 to uint32 (for max over packed keys); -0 is
+// folded onto +0 first so that equal values compare equal.
+__device__ __forceinline__ uint32_t orderable(float f)
+{
+    uint32_t b = __float_as_uint(f + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Argmax key: larger value wins, then the lower index (stored inverted).
+__device__ __forceinline__ uint64_t argmax_key(float f, uint32_t idx)
+{
+    return ((uint64_t)orderable(f) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    uint32_t lo = __shfl_xor((uint32_t)v, m);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+} // namespace archead

@@ -1,0 +1,29 @@
+// kernels.hpp -- host-side launchers of the ARCHead forward kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "layout.hpp"
+
+namespace archead {
+
+// a1: t = X (sB o B8)^T and s = X (sD o D8)^T as bf16 hi/lo pairs, and the
+// per-(group, row) X sums the residual kernels need.
+hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
+
+// a2-S: register-dequantised MFMA over vocabulary tiles (any M, W streamed
+// once per 32 hidden states).  logits may be null; part may be null.
+hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
+                               bool want_argmax, hipStream_t st, int64_t *n_part_out);
+
+// a2-G: VALU dot2 GEMV with wave shuffles (M <= 4).
+hipError_t launch_vtile_gemv(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
+                             bool want_argmax, hipStream_t st, int64_t *n_part_out);
+
+// number of argmax partials per row the given path writes
+int64_t skinny_n_part(const DevHead &h, int64_t M);
+int64_t gemv_n_part(const DevHead &h, int64_t M);
+
+// a3: reduce the argmax partial keys of each row to an index.
+hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st);
+
+} // namespace archead

@@ -1,0 +1,115 @@
+// layout.hpp -- device layout of a packed ARCHead head on gfx950.
+//
+// The packed module of the ARCHead paper (section 3.3) registers the SC4
+// INT4 residual with its fp16 group scales, the 5-bit / 8-bit core factors
+// with their scales, and the INT8 correction factors.  This file fixes how
+// those fields sit in HBM so that the vocabulary-tile kernels read them with
+// fully coalesced 16-byte loads and need no shuffles to feed MFMA.
+//
+// Vocabulary rows are grouped in blocks of 16 ("v-blocks"); the hidden
+// dimension in K-steps of 32.  One K-step of one v-block is exactly the
+// B operand of a v_mfma_f32_16x16x32 instruction: lane l (0..63) holds row
+// (l % 16) of the block and the 8 consecutive columns 8*(l/16) .. +7 of the
+// K-step.  Every field below stores, per (v-block, K-step), 64 lanes' worth
+// of that operand back to back.
+//
+//  r4   uint32 [nvb][d/128][64][4]   SC4 residual.  Dword s of lane l in
+//       K-chunk c covers columns 128c + 32s + 8(l/16) + e, e = 0..7; value
+//       e sits in nibble (e>>1) + 4(e&1) as offset binary (q + 8).  Masking
+//       nibbles (p, p+4) with 0x000F000F therefore yields the column pair
+//       (2p, 2p+1) in the two 16-bit halves, in order.
+//  sr   uint16 [nvb][G][16]          fp16 residual scales, G = d/g.
+//  a5n  uint32 [nvb][kst][64]        low 4 bits of (a + 16) for the 5-bit
+//       core factor, nibble order as r4; kst = ceil(k/32) K-steps.
+//  a5h  uint32 [nvb][ceil(kst/4)][64] bit 4 of (a + 16).  For K-step
+//       4q4 + q, column pair p, half h, the bit sits at (4 + 4q + p + 16h)
+//       mod 32, so rotating the dword right by 4q + p lands the two bits of
+//       the pair at positions 4 and 20.
+//  c8   uint32 [nvb][rst][64][2]     correction factor C8 (quantised A_w) as
+//       offset-binary bytes (c ^ 0x80), byte e of the lane's 8 columns in
+//       natural order; rst = ceil(r/32).
+//  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
+//  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
+//  d8   int8   [r][d], sd float [r][G]  quantised B_w and its group scales.
+// Padding rows (v >= V) and padding columns (k..kst*32, r..rst*32) hold the
+// code of zero with zero scales.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace archead {
+
+constexpr int kVB = 16;      // vocabulary rows per v-block
+constexpr int kKStep = 32;   // K columns per MFMA K-step
+constexpr int kKChunk = 128; // K columns per 16-byte lane load of r4
+
+struct Shape {
+    int64_t V, d, k, r, g;
+    __host__ __device__ int64_t nvb() const { return (V + kVB - 1) / kVB; }
+    __host__ __device__ int64_t G() const { return d / g; }
+    __host__ __device__ int64_t nkc() const { return d / kKChunk; }
+    __host__ __device__ int64_t kst() const { return (k + kKStep - 1) / kKStep; }
+    __host__ __device__ int64_t rst() const { return (r + kKStep - 1) / kKStep; }
+    __host__ __device__ int64_t kpad() const { return kst() * kKStep; }
+    __host__ __device__ int64_t rpad() const { return rst() * kKStep; }
+    __host__ __device__ int64_t a5h_groups() const { return (kst() + 3) / 4; }
+
+    // element counts of each device array
+    __host__ __device__ size_t n_r4() const { return (size_t)nvb() * nkc() * 64 * 4; }      // uint32
+    __host__ __device__ size_t n_sr() const { return (size_t)nvb() * G() * kVB; }           // uint16
+    __host__ __device__ size_t n_a5n() const { return (size_t)nvb() * kst() * 64; }         // uint32
+    __host__ __device__ size_t n_a5h() const { return (size_t)nvb() * a5h_groups() * 64; }  // uint32
+    __host__ __device__ size_t n_c8() const { return (size_t)nvb() * rst() * 64 * 2; }      // uint32
+    __host__ __device__ size_t n_rows() const { return (size_t)nvb() * kVB; }               // sa, sc
+};
+
+// Raw device pointers of one loaded head (all device memory).
+struct DevHead {
+    Shape s;
+    const uint32_t *r4;
+    const uint16_t *sr;
+    const uint32_t *a5n;
+    const uint32_t *a5h;
+    const uint32_t *c8;
+    const uint16_t *sa;
+    const uint16_t *sc;
+    const int8_t *b8;
+    const float *sb;
+    const int8_t *d8;
+    const float *sd;
+};
+
+// Per-call workspace, written by the projection kernel and read by the
+// vocabulary-tile kernels.  Mp = M rounded up to a multiple of 32.
+struct Work {
+    int64_t M, Mp;
+    uint16_t *t16;     // [2][Mp][kpad] bf16 hi/lo of t = X (sB o B8)^T
+    uint16_t *s16;     // [2][Mp][rpad] bf16 hi/lo of s = X (sD o D8)^T
+    float *xsneg;      // [G][Mp]  -136 * sum_{j in group} X[m, j]
+    uint64_t *part;    // [M][n_part] argmax partial keys
+    int64_t n_part;
+};
+
+// Host relayout (pack.cpp).  Inputs in the canonical host layout; outputs are
+// host buffers in the device layout, sized by Shape::n_*.
+struct HostDevImage {
+    uint32_t *r4;
+    uint16_t *sr;
+    uint32_t *a5n;
+    uint32_t *a5h;
+    uint32_t *c8;
+    uint16_t *sa;
+    uint16_t *sc;
+    float *sb;
+    float *sd;
+};
+
+void relayout(const Shape &s, const int8_t *A5, const uint16_t *sA, const uint16_t *sB,
+              const uint8_t *R4, const uint16_t *sR, const int8_t *C8, const uint16_t *sC,
+              const uint16_t *sD, const HostDevImage &out, int n_threads);
+
+float half_to_float(uint16_t h);
+
+} // namespace archead
