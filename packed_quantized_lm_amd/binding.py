@@ -53,6 +53,9 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m packed_quantized_lm_amd.build`")
+    # torch first: its HIP runtime is then the one the library binds to (same
+    # soname), so torch's streams and allocations are valid inside the library
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -331,14 +331,14 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
     HIP_TRY(launch_proj(h->dev, w, Xb, st));
-    int64_t n_part = 0;
+    bool argmax_done = false;
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
-    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax != nullptr, st, &n_part));
+    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st, &argmax_done));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
-    if (argmax)
-        HIP_TRY(launch_argmax(w, n_part, argmax, st));
+    if (argmax && !argmax_done)
+        HIP_TRY(launch_argmax(w, skinny_n_part(h->dev, M), argmax, st));
     return ARCHEAD_OK;
 }
 

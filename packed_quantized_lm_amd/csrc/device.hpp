@@ -36,8 +36,32 @@ __device__ __forceinline__ uint32_t rotr(uint32_t x, uint32_t n)
     return __builtin_amdgcn_alignbit(x, x, n);
 }
 
+// A uniform constant held in a VGPR.  With the magic exponent in a VGPR and
+// the mask in an SGPR the compiler emits one v_and_or_b32 per column pair
+// (VOP3 takes no literal); given two literals it emits v_and + v_or.  Only
+// this move is opaque: every instruction that feeds an MFMA is still the
+// compiler's own, so its hazard tracking stays intact.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c)
+{
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
 // Residual dword (8 offset-binary nibbles, slot order of layout.hpp) ->
-// 8 bf16 values q + 136, columns in natural order.
+// 8 bf16 values q + 136, columns in natural order.  c must be
+// vgpr_const(kBf16Magic).
+__device__ __forceinline__ u32x4 r4_bf16(uint32_t w, uint32_t c)
+{
+    const uint32_t m = 0x000F000Fu;
+    u32x4 o;
+    o.x = (w & m) | c;
+    o.y = ((w >> 4) & m) | c;
+    o.z = ((w >> 8) & m) | c;
+    o.w = ((w >> 12) & m) | c;
+    return o;
+}
+
 __device__ __forceinline__ u32x4 r4_bf16(uint32_t w)
 {
     u32x4 o;

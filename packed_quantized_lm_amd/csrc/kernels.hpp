@@ -12,16 +12,13 @@ hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipSt
 
 // a2-S: register-dequantised MFMA over vocabulary tiles (any M, W streamed
 // once per 32 hidden states).  logits may be null; part may be null.
+// argmax may be null.  *argmax_done is set when the kernel also produced the
+// final indices (small M); otherwise launch_argmax must follow.
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                               bool want_argmax, hipStream_t st, int64_t *n_part_out);
+                               int32_t *argmax, hipStream_t st, bool *argmax_done);
 
-// a2-G: VALU dot2 GEMV with wave shuffles (M <= 4).
-hipError_t launch_vtile_gemv(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                             bool want_argmax, hipStream_t st, int64_t *n_part_out);
-
-// number of argmax partials per row the given path writes
+// number of argmax partials per row the skinny path writes
 int64_t skinny_n_part(const DevHead &h, int64_t M);
-int64_t gemv_n_part(const DevHead &h, int64_t M);
 
 // a3: reduce the argmax partial keys of each row to an index.
 hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st);

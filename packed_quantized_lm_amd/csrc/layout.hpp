@@ -13,7 +13,11 @@
 // K-step.  Every field below stores, per (v-block, K-step), 64 lanes' worth
 // of that operand back to back.
 //
-//  r4   uint32 [nvb][d/128][64][4]   SC4 residual.  Dword s of lane l in
+//  r4   uint32 [d/128][nvb][64][4]   SC4 residual, K-chunk major: for one
+//       K-chunk the 1 KiB blocks of consecutive v-blocks are adjacent, so the
+//       waves streaming neighbouring v-blocks read one contiguous region at a
+//       time (v-block major order, with each wave's streams 32 KiB apart,
+//       measured about 1.5x slower on MI355X).  Dword s of lane l in
 //       K-chunk c covers columns 128c + 32s + 8(l/16) + e, e = 0..7; value
 //       e sits in nibble (e>>1) + 4(e&1) as offset binary (q + 8).  Masking
 //       nibbles (p, p+4) with 0x000F000F therefore yields the column pair
@@ -57,7 +61,7 @@ struct Shape {
     __host__ __device__ int64_t a5h_groups() const { return (kst() + 3) / 4; }
 
     // element counts of each device array
-    __host__ __device__ size_t n_r4() const { return (size_t)nvb() * nkc() * 64 * 4; }      // uint32
+    __host__ __device__ size_t n_r4() const { return (size_t)nkc() * nvb() * 64 * 4; }      // uint32
     __host__ __device__ size_t n_sr() const { return (size_t)nvb() * G() * kVB; }           // uint16
     __host__ __device__ size_t n_a5n() const { return (size_t)nvb() * kst() * 64; }         // uint32
     __host__ __device__ size_t n_a5h() const { return (size_t)nvb() * a5h_groups() * 64; }  // uint32

@@ -30,7 +30,7 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                      const HostDevImage &o, int64_t vb0, int64_t vb1)
 {
     const int64_t V = s.V, d = s.d, k = s.k, r = s.r, G = s.G();
-    const int64_t nkc = s.nkc(), kst = s.kst(), rst = s.rst(), ahg = s.a5h_groups();
+    const int64_t nvb = s.nvb(), nkc = s.nkc(), kst = s.kst(), rst = s.rst(), ahg = s.a5h_groups();
     for (int64_t vb = vb0; vb < vb1; ++vb) {
         for (int lane = 0; lane < 64; ++lane) {
             const int64_t row = vb * kVB + (lane & 15);
@@ -45,7 +45,7 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                         int q = live ? r4_value(R4, row, col, d) : 0;
                         w |= (uint32_t)((q + 8) & 0xF) << (4 * slot(e));
                     }
-                    o.r4[((vb * nkc + kc) * 64 + lane) * 4 + st] = w;
+                    o.r4[((kc * nvb + vb) * 64 + lane) * 4 + st] = w;
                 }
             }
             // 5-bit core factor: nibble plane + high-bit plane of (a + 16)
