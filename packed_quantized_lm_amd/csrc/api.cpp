@@ -57,6 +57,8 @@ struct archead_head {
     void *ws;           // workspace
     size_t ws_bytes;
     int64_t ws_M;       // largest M the workspace holds
+    float *ylog;        // M x V fp32 scratch logits for argmax-only calls (lazy)
+    int64_t ylog_M;
     int device;
 };
 
@@ -204,7 +206,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     };
     const size_t o_r4 = place(s.n_r4() * 4), o_sr = place(s.n_sr() * 2);
     const size_t o_a5n = place(s.n_a5n() * 4), o_a5h = place(s.n_a5h() * 4);
-    const size_t o_c8 = place(s.n_c8() * 4), o_sa = place(s.n_rows() * 2);
+    const size_t o_c8 = place(s.n_c8() * 4), o_lr = place(s.n_lr_words() * 4);
+    const size_t o_sa = place(s.n_rows() * 2);
     const size_t o_sc = place(s.n_rows() * 2), o_b8 = place(size_t(k) * d);
     const size_t o_sb = place(size_t(k) * 4), o_d8 = place(size_t(r) * d);
     const size_t o_sd = place(size_t(r) * s.G() * 4);
@@ -218,8 +221,9 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     }
     char *hb = host.data();
     HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_a5n),
-                     (uint32_t *)(hb + o_a5h), (uint32_t *)(hb + o_c8), (uint16_t *)(hb + o_sa),
-                     (uint16_t *)(hb + o_sc), (float *)(hb + o_sb), (float *)(hb + o_sd)};
+                     (uint32_t *)(hb + o_a5h), (uint32_t *)(hb + o_c8), (uint32_t *)(hb + o_lr),
+                     (uint16_t *)(hb + o_sa), (uint16_t *)(hb + o_sc), (float *)(hb + o_sb),
+                     (float *)(hb + o_sd)};
     relayout(s, A5, sA, sB, R4, sR, C8, sC, sD, img,
              (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency())));
     if (k > 0)
@@ -256,6 +260,7 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->dev.a5n = (const uint32_t *)(db + o_a5n);
     h->dev.a5h = (const uint32_t *)(db + o_a5h);
     h->dev.c8 = (const uint32_t *)(db + o_c8);
+    h->dev.lr = (const uint32_t *)(db + o_lr);
     h->dev.sa = (const uint16_t *)(db + o_sa);
     h->dev.sc = (const uint16_t *)(db + o_sc);
     h->dev.b8 = (const int8_t *)(db + o_b8);
@@ -267,6 +272,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->ws = nullptr;
     h->ws_bytes = 0;
     h->ws_M = 0;
+    h->ylog = nullptr;
+    h->ylog_M = 0;
     h->device = dev;
     st = grow_workspace(h, 1, stream);
     if (st != ARCHEAD_OK) {
@@ -334,7 +341,18 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     bool argmax_done = false;
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
-    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st, &argmax_done));
+    if (!logits && h->ylog_M < M) {
+        HIP_TRY(hipStreamSynchronize(st));
+        if (h->ylog)
+            HIP_TRY(hipFree(h->ylog));
+        h->ylog = nullptr;
+        h->ylog_M = 0;
+        hipError_t ea = hipMalloc((void **)&h->ylog, size_t(M) * h->s.V * sizeof(float));
+        if (ea != hipSuccess)
+            return fail(ARCHEAD_ENOMEM, std::string("scratch logits hipMalloc: ") + hipGetErrorString(ea));
+        h->ylog_M = M;
+    }
+    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, h->ylog, argmax, st, &argmax_done));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
     if (argmax && !argmax_done)
@@ -398,7 +416,7 @@ archead_status archead_device_bytes(archead_t h, uint64_t *bytes)
     g_err.clear();
     if (!live(h) || !bytes)
         return fail(ARCHEAD_EINVAL, "invalid handle or NULL output");
-    *bytes = h->block_bytes + h->ws_bytes;
+    *bytes = h->block_bytes + h->ws_bytes + size_t(h->ylog_M) * h->s.V * sizeof(float);
     return ARCHEAD_OK;
 }
 
@@ -417,6 +435,8 @@ archead_status archead_free(archead_t h)
     hipError_t e = hipDeviceSynchronize();
     if (h->ws)
         (void)hipFree(h->ws);
+    if (h->ylog)
+        (void)hipFree(h->ylog);
     if (h->block)
         (void)hipFree(h->block);
     h->magic = 0;

@@ -10,12 +10,14 @@ namespace archead {
 // per-(group, row) X sums the residual kernels need.
 hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 
-// a2-S: register-dequantised MFMA over vocabulary tiles (any M, W streamed
-// once per 32 hidden states).  logits may be null; part may be null.
-// argmax may be null.  *argmax_done is set when the kernel also produced the
-// final indices (small M); otherwise launch_argmax must follow.
+// a2-S: register-dequantised MFMA over vocabulary tiles (any M; the packed
+// fields are streamed once per 32 hidden states): a residual-stream kernel
+// then a low-rank + epilogue kernel.  logits may be null, in which case
+// scratch (M x V fp32) carries the residual term between the two.  argmax may
+// be null; when set, the per-workgroup partials are left in w.part and
+// launch_argmax must follow (*argmax_done reports whether it already ran).
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                               int32_t *argmax, hipStream_t st, bool *argmax_done);
+                               float *scratch, int32_t *argmax, hipStream_t st, bool *argmax_done);
 
 // number of argmax partials per row the skinny path writes
 int64_t skinny_n_part(const DevHead &h, int64_t M);

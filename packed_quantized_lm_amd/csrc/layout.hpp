@@ -32,6 +32,13 @@
 //  c8   uint32 [nvb][rst][64][2]     correction factor C8 (quantised A_w) as
 //       offset-binary bytes (c ^ 0x80), byte e of the lane's 8 columns in
 //       natural order; rst = ceil(r/32).
+//  lr   uint32 [n_lr][nvb][64][4]   the same codes again as one 1 KiB-per-
+//       lane-chunk stream, K-chunk major like r4, so that the streaming kernel
+//       reads the low-rank codes through the same pipeline as the residual.
+//       Chunks 0 .. na-1 (na = ceil(kst/3)): dwords 0..2 = a5n of K-steps
+//       3j .. 3j+2, dword 3 = their high bits (K-step 3j+q at the positions
+//       of q in a5h); chunks na .. na+nc-1 (nc = ceil(rst/2)): dwords (0,1) and
+//       (2,3) = c8 of K-steps 2j and 2j+1.  Missing K-steps hold zero codes.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
 //  d8   int8   [r][d], sd float [r][G]  quantised B_w and its group scales.
@@ -59,6 +66,9 @@ struct Shape {
     __host__ __device__ int64_t kpad() const { return kst() * kKStep; }
     __host__ __device__ int64_t rpad() const { return rst() * kKStep; }
     __host__ __device__ int64_t a5h_groups() const { return (kst() + 3) / 4; }
+    __host__ __device__ int64_t lr_na() const { return (kst() + 2) / 3; }  // A5 chunks
+    __host__ __device__ int64_t lr_nc() const { return (rst() + 1) / 2; }  // C8 chunks
+    __host__ __device__ int64_t n_lr() const { return lr_na() + lr_nc(); }
 
     // element counts of each device array
     __host__ __device__ size_t n_r4() const { return (size_t)nkc() * nvb() * 64 * 4; }      // uint32
@@ -67,6 +77,7 @@ struct Shape {
     __host__ __device__ size_t n_a5h() const { return (size_t)nvb() * a5h_groups() * 64; }  // uint32
     __host__ __device__ size_t n_c8() const { return (size_t)nvb() * rst() * 64 * 2; }      // uint32
     __host__ __device__ size_t n_rows() const { return (size_t)nvb() * kVB; }               // sa, sc
+    __host__ __device__ size_t n_lr_words() const { return (size_t)n_lr() * nvb() * 64 * 4; } // uint32
 };
 
 // Raw device pointers of one loaded head (all device memory).
@@ -77,6 +88,7 @@ struct DevHead {
     const uint32_t *a5n;
     const uint32_t *a5h;
     const uint32_t *c8;
+    const uint32_t *lr;
     const uint16_t *sa;
     const uint16_t *sc;
     const int8_t *b8;
@@ -104,6 +116,7 @@ struct HostDevImage {
     uint32_t *a5n;
     uint32_t *a5h;
     uint32_t *c8;
+    uint32_t *lr;
     uint16_t *sa;
     uint16_t *sc;
     float *sb;

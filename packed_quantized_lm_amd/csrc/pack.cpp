@@ -68,6 +68,41 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                 }
                 o.a5h[(vb * ahg + g4) * 64 + lane] = hw;
             }
+            // the low-rank codes again as the chunked stream "lr"
+            {
+                const int64_t na = s.lr_na(), nc = s.lr_nc();
+                auto nib_word = [&](int64_t st, uint32_t *hbits, int q) {
+                    uint32_t nw = 0;
+                    for (int e = 0; e < 8; ++e) {
+                        int64_t col = st * kKStep + 8 * quarter + e;
+                        int a = (live && col < k) ? A5[row * k + col] : 0;
+                        uint32_t u5 = (uint32_t)(a + 16);
+                        nw |= (u5 & 0xF) << (4 * slot(e));
+                        int bit = (4 + 4 * q + (e >> 1) + 16 * (e & 1)) & 31;
+                        *hbits |= (u5 >> 4) << bit;
+                    }
+                    return nw;
+                };
+                for (int64_t j = 0; j < na; ++j) {
+                    uint32_t hb = 0, w[4];
+                    for (int q = 0; q < 3; ++q)
+                        w[q] = nib_word(3 * j + q, &hb, q);
+                    w[3] = hb;
+                    for (int q = 0; q < 4; ++q)
+                        o.lr[((j * nvb + vb) * 64 + lane) * 4 + q] = w[q];
+                }
+                for (int64_t j = 0; j < nc; ++j) {
+                    uint32_t w[4] = {0, 0, 0, 0};
+                    for (int h = 0; h < 2; ++h)
+                        for (int e = 0; e < 8; ++e) {
+                            int64_t col = (2 * j + h) * kKStep + 8 * quarter + e;
+                            int c = (live && col < r) ? C8[row * r + col] : 0;
+                            w[2 * h + (e >> 2)] |= (uint32_t)((uint8_t)c ^ 0x80u) << (8 * (e & 3));
+                        }
+                    for (int q = 0; q < 4; ++q)
+                        o.lr[(((na + j) * nvb + vb) * 64 + lane) * 4 + q] = w[q];
+                }
+            }
             // INT8 correction factor A_w, offset-binary bytes
             for (int64_t st = 0; st < rst; ++st) {
                 uint32_t w[2] = {0, 0};
