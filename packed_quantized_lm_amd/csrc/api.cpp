@@ -57,8 +57,6 @@ struct archead_head {
     void *ws;           // workspace
     size_t ws_bytes;
     int64_t ws_M;       // largest M the workspace holds
-    float *ylog;        // M x V fp32 scratch logits for argmax-only calls (lazy)
-    int64_t ylog_M;
     int device;
 };
 
@@ -272,8 +270,6 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->ws = nullptr;
     h->ws_bytes = 0;
     h->ws_M = 0;
-    h->ylog = nullptr;
-    h->ylog_M = 0;
     h->device = dev;
     st = grow_workspace(h, 1, stream);
     if (st != ARCHEAD_OK) {
@@ -338,24 +334,12 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
     HIP_TRY(launch_proj(h->dev, w, Xb, st));
-    bool argmax_done = false;
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
-    if (!logits && h->ylog_M < M) {
-        HIP_TRY(hipStreamSynchronize(st));
-        if (h->ylog)
-            HIP_TRY(hipFree(h->ylog));
-        h->ylog = nullptr;
-        h->ylog_M = 0;
-        hipError_t ea = hipMalloc((void **)&h->ylog, size_t(M) * h->s.V * sizeof(float));
-        if (ea != hipSuccess)
-            return fail(ARCHEAD_ENOMEM, std::string("scratch logits hipMalloc: ") + hipGetErrorString(ea));
-        h->ylog_M = M;
-    }
-    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, h->ylog, argmax, st, &argmax_done));
+    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
-    if (argmax && !argmax_done)
+    if (argmax)
         HIP_TRY(launch_argmax(w, skinny_n_part(h->dev, M), argmax, st));
     return ARCHEAD_OK;
 }
@@ -416,7 +400,7 @@ archead_status archead_device_bytes(archead_t h, uint64_t *bytes)
     g_err.clear();
     if (!live(h) || !bytes)
         return fail(ARCHEAD_EINVAL, "invalid handle or NULL output");
-    *bytes = h->block_bytes + h->ws_bytes + size_t(h->ylog_M) * h->s.V * sizeof(float);
+    *bytes = h->block_bytes + h->ws_bytes;
     return ARCHEAD_OK;
 }
 
@@ -435,8 +419,6 @@ archead_status archead_free(archead_t h)
     hipError_t e = hipDeviceSynchronize();
     if (h->ws)
         (void)hipFree(h->ws);
-    if (h->ylog)
-        (void)hipFree(h->ylog);
     if (h->block)
         (void)hipFree(h->block);
     h->magic = 0;

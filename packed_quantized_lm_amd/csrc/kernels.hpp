@@ -10,14 +10,13 @@ namespace archead {
 // per-(group, row) X sums the residual kernels need.
 hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 
-// a2-S: register-dequantised MFMA over vocabulary tiles (any M; the packed
-// fields are streamed once per 32 hidden states): a residual-stream kernel
-// then a low-rank + epilogue kernel.  logits may be null, in which case
-// scratch (M x V fp32) carries the residual term between the two.  argmax may
-// be null; when set, the per-workgroup partials are left in w.part and
-// launch_argmax must follow (*argmax_done reports whether it already ran).
+// a2-S: one streaming kernel over vocabulary tiles (any M; the packed codes
+// are streamed once per 32 hidden states): per v-block the low-rank codes,
+// then the SC4 residual, then the logits (if logits is not null) and, if
+// argmax is not null, the per-workgroup top-1 partials in w.part, which
+// launch_argmax reduces.
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                               float *scratch, int32_t *argmax, hipStream_t st, bool *argmax_done);
+                               int32_t *argmax, hipStream_t st);
 
 // number of argmax partials per row the skinny path writes
 int64_t skinny_n_part(const DevHead &h, int64_t M);

@@ -38,7 +38,8 @@
 //       Chunks 0 .. na-1 (na = ceil(kst/3)): dwords 0..2 = a5n of K-steps
 //       3j .. 3j+2, dword 3 = their high bits (K-step 3j+q at the positions
 //       of q in a5h); chunks na .. na+nc-1 (nc = ceil(rst/2)): dwords (0,1) and
-//       (2,3) = c8 of K-steps 2j and 2j+1.  Missing K-steps hold zero codes.
+//       (2,3) = c8 of K-steps 2j and 2j+1, for j up to n_lr - na (the count is
+//       padded to even).  Missing K-steps hold the code of zero.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
 //  d8   int8   [r][d], sd float [r][G]  quantised B_w and its group scales.
@@ -68,7 +69,10 @@ struct Shape {
     __host__ __device__ int64_t a5h_groups() const { return (kst() + 3) / 4; }
     __host__ __device__ int64_t lr_na() const { return (kst() + 2) / 3; }  // A5 chunks
     __host__ __device__ int64_t lr_nc() const { return (rst() + 1) / 2; }  // C8 chunks
-    __host__ __device__ int64_t n_lr() const { return lr_na() + lr_nc(); }
+    // total low-rank chunks, rounded up to even so that the residual chunks
+    // start in the first of the two prefetch buffers (the pad chunk is a
+    // correction chunk whose K-steps all lie beyond rst)
+    __host__ __device__ int64_t n_lr() const { return (lr_na() + lr_nc() + 1) / 2 * 2; }
 
     // element counts of each device array
     __host__ __device__ size_t n_r4() const { return (size_t)nkc() * nvb() * 64 * 4; }      // uint32

@@ -70,7 +70,7 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
             }
             // the low-rank codes again as the chunked stream "lr"
             {
-                const int64_t na = s.lr_na(), nc = s.lr_nc();
+                const int64_t na = s.lr_na(), nc = s.n_lr() - na;
                 auto nib_word = [&](int64_t st, uint32_t *hbits, int q) {
                     uint32_t nw = 0;
                     for (int e = 0; e < 8; ++e) {
