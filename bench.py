@@ -51,14 +51,32 @@ def path_flops(V, d, k, r, M):
     return 2 * M * (V * d + V * k + V * r + k * d + r * d)
 
 
+KERNEL_SOURCES = ("vtile.hip", "device.hpp", "layout.hpp", "pack.cpp")
+
+
+def kernel_source_hash():
+    """sha256 over the sources that define the vocabulary-tile kernel and the
+    layout it reads."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "packed_quantized_lm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def read_traffic(kernel_tag, workload):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if
-    one exists for this kernel and workload (profiles/<kernel>_<workload>_counters.json)."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>_counters.json: FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the counter reads for a plain copy of known size).
+    None when no summary exists or when it was taken on other kernel sources."""
     p = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_counters.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         data = json.load(fh)
+    if data.get("source_sha256") != kernel_source_hash():
+        return None
     return data.get("hbm_bytes_per_launch")
 
 
@@ -138,6 +156,24 @@ def cpu_baseline(name="qwen_m1", budget_s=15.0):
                       f"({t:.1f} s), scaled to the full head"}
 
 
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of nbytes, run steps times: the known
+    read and write volume against which the HBM byte counters (FETCH_SIZE,
+    WRITE_SIZE) of a profiled run are scaled."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": 4 * n, "steps": steps, "s_per_copy": dt,
+                      "GBs_read_plus_write": 8 * n / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +184,9 @@ def main():
     ap.add_argument("--path", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many bytes "
+                         "--steps times (calibration of the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the packed head's "
@@ -156,6 +195,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
     from packed_quantized_lm_amd import load_library
     load_library()
 
