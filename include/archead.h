@@ -81,7 +81,7 @@ typedef enum archead_path {
  * correction factors and shape metadata; the dense V x D head is not kept).
  *
  * V, d, k, r, g  shape (see above).  Supported: V >= 1, V < 2^31;
- *                d a multiple of 128; g a multiple of 32 dividing d;
+ *                d a multiple of 128 in [128, 2^20]; g a multiple of 32 dividing d;
  *                0 <= k <= 4096, 0 <= r <= 4096 (k = 0 or r = 0 drop the
  *                core or the correction term; the corresponding pointers
  *                may then be NULL).  Otherwise ARCHEAD_ESHAPE.
@@ -114,9 +114,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
 archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream);
 
 /*
- * archead_forward -- logits = X W_hat^T, factored as in eq 7 (ARCHead paper
- * section 3.2; "the inference computation is factored, avoiding the
- * reconstruction of a dense matrix").
+ * archead_forward -- logits = X W_hat^T, evaluated factored as in eq 7
+ * (ARCHead paper section 3.2): the dense V x d head is never formed.
  *
  * M        number of hidden states, 0 <= M <= 2^20 (M = 0 is a no-op that
  *          succeeds whatever X and logits are).

@@ -2,7 +2,7 @@
 
 ARCHead paper, section 3.2, eq 3: Q_b is b-bit group quantisation (Q5 for the
 left core factor, Q8 for the right one, SC4 for the packed signed INT4
-residual "with quantised group scales"); the text after eq 7 stores both
+residual, whose group scales are stored quantised); the text after eq 7 stores both
 correction factors with row/group INT8 quantisation; section 3.3 lists the
 scales as FP16/BF16.  The paper does not spell the quantiser out.  Reading
 taken here (each point listed in the design notes):

@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, part, total;
+    size_t t16, s16, xsneg, x16, xsc, part, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -78,7 +78,7 @@ int64_t max_n_part(const Shape &s)
 {
     DevHead tmp{};
     tmp.s = s;
-    return std::max<int64_t>(skinny_n_part(tmp, 1), 1);
+    return std::max<int64_t>(std::max(skinny_n_part(tmp, 1), lds_n_part(tmp, 1)), 1);
 }
 
 WsLayout ws_layout(const Shape &s, int64_t Mmax)
@@ -92,6 +92,10 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(2) * Mp * s.rpad() * 2);
     L.xsneg = off;
     off = align_up(off + size_t(s.G()) * Mp * 4);
+    L.x16 = off;
+    off = align_up(off + size_t(Mp) * s.d * 2);
+    L.xsc = off;
+    off = align_up(off + size_t(Mp) * 2 * 4);
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
     L.total = off;
@@ -132,6 +136,8 @@ Work make_work(archead_t h, int64_t M)
     w.t16 = (uint16_t *)(b + L.t16);
     w.s16 = (uint16_t *)(b + L.s16);
     w.xsneg = (float *)(b + L.xsneg);
+    w.x16 = (uint16_t *)(b + L.x16);
+    w.xsc = (float *)(b + L.xsc);
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
     return w;
@@ -141,8 +147,8 @@ archead_status validate_shape(int64_t V, int64_t d, int64_t k, int64_t r, int64_
 {
     if (V < 1 || V >= (int64_t(1) << 31))
         return fail(ARCHEAD_ESHAPE, "V must satisfy 1 <= V < 2^31");
-    if (d < kKChunk || d % kKChunk)
-        return fail(ARCHEAD_ESHAPE, "d must be a positive multiple of 128");
+    if (d < kKChunk || d % kKChunk || d > (int64_t(1) << 20))
+        return fail(ARCHEAD_ESHAPE, "d must be a multiple of 128 in [128, 2^20]");
     if (g < kKStep || g % kKStep || d % g)
         return fail(ARCHEAD_ESHAPE, "g must be a multiple of 32 that divides d");
     if (k < 0 || k > 4096 || r < 0 || r > 4096)
@@ -203,8 +209,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
         return o;
     };
     const size_t o_r4 = place(s.n_r4() * 4), o_sr = place(s.n_sr() * 2);
-    const size_t o_a5n = place(s.n_a5n() * 4), o_a5h = place(s.n_a5h() * 4);
-    const size_t o_c8 = place(s.n_c8() * 4), o_lr = place(s.n_lr_words() * 4);
+    const size_t o_srp = place(s.n_sr() * 2), o_rsc = place(s.n_rows() * 4);
+    const size_t o_lr = place(s.n_lr_words() * 4);
     const size_t o_sa = place(s.n_rows() * 2);
     const size_t o_sc = place(s.n_rows() * 2), o_b8 = place(size_t(k) * d);
     const size_t o_sb = place(size_t(k) * 4), o_d8 = place(size_t(r) * d);
@@ -218,10 +224,9 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
         return fail(ARCHEAD_ENOMEM, "host staging allocation failed");
     }
     char *hb = host.data();
-    HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_a5n),
-                     (uint32_t *)(hb + o_a5h), (uint32_t *)(hb + o_c8), (uint32_t *)(hb + o_lr),
-                     (uint16_t *)(hb + o_sa), (uint16_t *)(hb + o_sc), (float *)(hb + o_sb),
-                     (float *)(hb + o_sd)};
+    HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_lr),
+                     (uint16_t *)(hb + o_srp), (float *)(hb + o_rsc), (uint16_t *)(hb + o_sa),
+                     (uint16_t *)(hb + o_sc), (float *)(hb + o_sb), (float *)(hb + o_sd)};
     relayout(s, A5, sA, sB, R4, sR, C8, sC, sD, img,
              (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency())));
     if (k > 0)
@@ -255,10 +260,9 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->dev.s = s;
     h->dev.r4 = (const uint32_t *)(db + o_r4);
     h->dev.sr = (const uint16_t *)(db + o_sr);
-    h->dev.a5n = (const uint32_t *)(db + o_a5n);
-    h->dev.a5h = (const uint32_t *)(db + o_a5h);
-    h->dev.c8 = (const uint32_t *)(db + o_c8);
     h->dev.lr = (const uint32_t *)(db + o_lr);
+    h->dev.srp = (const uint16_t *)(db + o_srp);
+    h->dev.rsc = (const float *)(db + o_rsc);
     h->dev.sa = (const uint16_t *)(db + o_sa);
     h->dev.sc = (const uint16_t *)(db + o_sc);
     h->dev.b8 = (const int8_t *)(db + o_b8);
@@ -327,20 +331,27 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
 
     int chosen = path;
     if (chosen == ARCHEAD_PATH_AUTO)
-        chosen = ARCHEAD_PATH_SKINNY;
-    if (chosen != ARCHEAD_PATH_SKINNY)
+        chosen = M >= kLdsMinM ? ARCHEAD_PATH_LDS : ARCHEAD_PATH_SKINNY;
+    if (chosen != ARCHEAD_PATH_SKINNY && chosen != ARCHEAD_PATH_LDS)
         return fail(ARCHEAD_EINVAL, "path not available in this build");
 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
     HIP_TRY(launch_proj(h->dev, w, Xb, st));
+    if (chosen == ARCHEAD_PATH_LDS)
+        HIP_TRY(launch_prep_x16(h->dev, w, Xb, st));
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
-    HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st));
+    if (chosen == ARCHEAD_PATH_LDS)
+        HIP_TRY(launch_vtile_lds(h->dev, w, logits, argmax, st));
+    else
+        HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
-    if (argmax)
-        HIP_TRY(launch_argmax(w, skinny_n_part(h->dev, M), argmax, st));
+    if (argmax) {
+        const int64_t n_part = chosen == ARCHEAD_PATH_LDS ? lds_n_part(h->dev, M) : skinny_n_part(h->dev, M);
+        HIP_TRY(launch_argmax(w, n_part, argmax, st));
+    }
     return ARCHEAD_OK;
 }
 

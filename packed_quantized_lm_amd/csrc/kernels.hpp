@@ -21,6 +21,19 @@ hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *
 // number of argmax partials per row the skinny path writes
 int64_t skinny_n_part(const DevHead &h, int64_t M);
 
+// a2-L: LDS-staged MFMA over [128 hidden states x 512 vocabulary rows] tiles
+// for large M.  Needs launch_prep_x16 first (after launch_proj).  The SC4
+// term is computed in fp16 MFMA with sR * R4 rounded once to fp16; the
+// low-rank terms use exact integer bf16 codes against the hi/lo parts of t
+// and s.  Argmax partials as for a2-S.
+hipError_t launch_prep_x16(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
+hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int32_t *argmax,
+                            hipStream_t st);
+int64_t lds_n_part(const DevHead &h, int64_t M);
+
+// smallest M for which the automatic choice takes a2-L
+constexpr int64_t kLdsMinM = 128;
+
 // a3: reduce the argmax partial keys of each row to an index.
 hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st);
 

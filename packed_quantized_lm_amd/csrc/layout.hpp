@@ -23,23 +23,23 @@
 //       nibbles (p, p+4) with 0x000F000F therefore yields the column pair
 //       (2p, 2p+1) in the two 16-bit halves, in order.
 //  sr   uint16 [nvb][G][16]          fp16 residual scales, G = d/g.
-//  a5n  uint32 [nvb][kst][64]        low 4 bits of (a + 16) for the 5-bit
-//       core factor, nibble order as r4; kst = ceil(k/32) K-steps.
-//  a5h  uint32 [nvb][ceil(kst/4)][64] bit 4 of (a + 16).  For K-step
-//       4q4 + q, column pair p, half h, the bit sits at (4 + 4q + p + 16h)
-//       mod 32, so rotating the dword right by 4q + p lands the two bits of
-//       the pair at positions 4 and 20.
-//  c8   uint32 [nvb][rst][64][2]     correction factor C8 (quantised A_w) as
-//       offset-binary bytes (c ^ 0x80), byte e of the lane's 8 columns in
-//       natural order; rst = ceil(r/32).
-//  lr   uint32 [n_lr][nvb][64][4]   the same codes again as one 1 KiB-per-
-//       lane-chunk stream, K-chunk major like r4, so that the streaming kernel
-//       reads the low-rank codes through the same pipeline as the residual.
-//       Chunks 0 .. na-1 (na = ceil(kst/3)): dwords 0..2 = a5n of K-steps
-//       3j .. 3j+2, dword 3 = their high bits (K-step 3j+q at the positions
-//       of q in a5h); chunks na .. na+nc-1 (nc = ceil(rst/2)): dwords (0,1) and
-//       (2,3) = c8 of K-steps 2j and 2j+1, for j up to n_lr - na (the count is
-//       padded to even).  Missing K-steps hold the code of zero.
+//  lr   uint32 [n_lr][nvb][64][4]   the low-rank codes (5-bit core factor A5
+//       and INT8 correction factor C8) as a stream of 1 KiB v-block chunks,
+//       K-chunk major like r4, so that the streaming kernel reads them through
+//       the same pipeline as the residual.  kst = ceil(k/32), rst = ceil(r/32).
+//       Chunks j = 0 .. na-1 (na = ceil(kst/3)) hold core K-steps 3j+q,
+//       q = 0..2: dword q = low 4 bits of (a + 16) in the nibble order of r4,
+//       dword 3 = bit 4 of (a + 16), for K-step q and column pair p, half h,
+//       at bit (4 + 4q + p + 16h) mod 32, so rotating it right by 4q + p
+//       lands the pair's two bits at positions 4 and 20.  Chunks na + j hold
+//       correction K-steps 2j and 2j+1: dwords (0,1) and (2,3) = the lane's 8
+//       columns as offset-binary bytes (c ^ 0x80) in natural order.  The chunk
+//       count n_lr is padded to even; K-steps beyond kst / rst hold the code
+//       of zero and are skipped.
+//  srp  uint16 [nvb][G][16]          sR * 2^e_v in fp16 (exact power-of-two
+//       rescale, e_v per row such that the row's largest group scale lies in
+//       [1, 2)); the large-M kernel multiplies residual codes by it in fp16.
+//  rsc  float  [nvb*16]              2^-e_v per row.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
 //  d8   int8   [r][d], sd float [r][G]  quantised B_w and its group scales.
@@ -66,7 +66,6 @@ struct Shape {
     __host__ __device__ int64_t rst() const { return (r + kKStep - 1) / kKStep; }
     __host__ __device__ int64_t kpad() const { return kst() * kKStep; }
     __host__ __device__ int64_t rpad() const { return rst() * kKStep; }
-    __host__ __device__ int64_t a5h_groups() const { return (kst() + 3) / 4; }
     __host__ __device__ int64_t lr_na() const { return (kst() + 2) / 3; }  // A5 chunks
     __host__ __device__ int64_t lr_nc() const { return (rst() + 1) / 2; }  // C8 chunks
     // total low-rank chunks, rounded up to even so that the residual chunks
@@ -77,9 +76,6 @@ struct Shape {
     // element counts of each device array
     __host__ __device__ size_t n_r4() const { return (size_t)nkc() * nvb() * 64 * 4; }      // uint32
     __host__ __device__ size_t n_sr() const { return (size_t)nvb() * G() * kVB; }           // uint16
-    __host__ __device__ size_t n_a5n() const { return (size_t)nvb() * kst() * 64; }         // uint32
-    __host__ __device__ size_t n_a5h() const { return (size_t)nvb() * a5h_groups() * 64; }  // uint32
-    __host__ __device__ size_t n_c8() const { return (size_t)nvb() * rst() * 64 * 2; }      // uint32
     __host__ __device__ size_t n_rows() const { return (size_t)nvb() * kVB; }               // sa, sc
     __host__ __device__ size_t n_lr_words() const { return (size_t)n_lr() * nvb() * 64 * 4; } // uint32
 };
@@ -89,10 +85,9 @@ struct DevHead {
     Shape s;
     const uint32_t *r4;
     const uint16_t *sr;
-    const uint32_t *a5n;
-    const uint32_t *a5h;
-    const uint32_t *c8;
     const uint32_t *lr;
+    const uint16_t *srp;
+    const float *rsc;
     const uint16_t *sa;
     const uint16_t *sc;
     const int8_t *b8;
@@ -108,6 +103,8 @@ struct Work {
     uint16_t *t16;     // [2][Mp][kpad] bf16 hi/lo of t = X (sB o B8)^T
     uint16_t *s16;     // [2][Mp][rpad] bf16 hi/lo of s = X (sD o D8)^T
     float *xsneg;      // [G][Mp]  -136 * sum_{j in group} X[m, j]
+    uint16_t *x16;     // [Mp][d]  fp16 of X[m, :] * 2^f_m (large-M path)
+    float *xsc;        // [Mp][2]  (2^-f_m, 2^f_m)
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;
 };
@@ -117,10 +114,9 @@ struct Work {
 struct HostDevImage {
     uint32_t *r4;
     uint16_t *sr;
-    uint32_t *a5n;
-    uint32_t *a5h;
-    uint32_t *c8;
     uint32_t *lr;
+    uint16_t *srp;
+    float *rsc;
     uint16_t *sa;
     uint16_t *sc;
     float *sb;
@@ -132,5 +128,6 @@ void relayout(const Shape &s, const int8_t *A5, const uint16_t *sA, const uint16
               const uint16_t *sD, const HostDevImage &out, int n_threads);
 
 float half_to_float(uint16_t h);
+uint16_t float_to_half(float f); // round to nearest even
 
 } // namespace archead

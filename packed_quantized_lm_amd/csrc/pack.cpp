@@ -4,6 +4,7 @@
 #include "layout.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -11,6 +12,8 @@
 namespace archead {
 
 float half_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+uint16_t float_to_half(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 namespace {
 
@@ -30,7 +33,7 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                      const HostDevImage &o, int64_t vb0, int64_t vb1)
 {
     const int64_t V = s.V, d = s.d, k = s.k, r = s.r, G = s.G();
-    const int64_t nvb = s.nvb(), nkc = s.nkc(), kst = s.kst(), rst = s.rst(), ahg = s.a5h_groups();
+    const int64_t nvb = s.nvb(), nkc = s.nkc();
     for (int64_t vb = vb0; vb < vb1; ++vb) {
         for (int lane = 0; lane < 64; ++lane) {
             const int64_t row = vb * kVB + (lane & 15);
@@ -48,27 +51,7 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                     o.r4[((kc * nvb + vb) * 64 + lane) * 4 + st] = w;
                 }
             }
-            // 5-bit core factor: nibble plane + high-bit plane of (a + 16)
-            for (int64_t g4 = 0; g4 < ahg; ++g4) {
-                uint32_t hw = 0;
-                for (int q = 0; q < 4; ++q) {
-                    int64_t st = g4 * 4 + q;
-                    if (st >= kst)
-                        break;
-                    uint32_t nw = 0;
-                    for (int e = 0; e < 8; ++e) {
-                        int64_t col = st * kKStep + 8 * quarter + e;
-                        int a = (live && col < k) ? A5[row * k + col] : 0;
-                        uint32_t u5 = (uint32_t)(a + 16);
-                        nw |= (u5 & 0xF) << (4 * slot(e));
-                        int bit = (4 + 4 * q + (e >> 1) + 16 * (e & 1)) & 31;
-                        hw |= (u5 >> 4) << bit;
-                    }
-                    o.a5n[(vb * kst + st) * 64 + lane] = nw;
-                }
-                o.a5h[(vb * ahg + g4) * 64 + lane] = hw;
-            }
-            // the low-rank codes again as the chunked stream "lr"
+            // low-rank chunk stream: core K-steps in threes, then correction K-steps in twos
             {
                 const int64_t na = s.lr_na(), nc = s.n_lr() - na;
                 auto nib_word = [&](int64_t st, uint32_t *hbits, int q) {
@@ -103,23 +86,21 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
                         o.lr[(((na + j) * nvb + vb) * 64 + lane) * 4 + q] = w[q];
                 }
             }
-            // INT8 correction factor A_w, offset-binary bytes
-            for (int64_t st = 0; st < rst; ++st) {
-                uint32_t w[2] = {0, 0};
-                for (int e = 0; e < 8; ++e) {
-                    int64_t col = st * kKStep + 8 * quarter + e;
-                    int c = (live && col < r) ? C8[row * r + col] : 0;
-                    w[e >> 2] |= (uint32_t)((uint8_t)c ^ 0x80u) << (8 * (e & 3));
-                }
-                o.c8[((vb * rst + st) * 64 + lane) * 2 + 0] = w[0];
-                o.c8[((vb * rst + st) * 64 + lane) * 2 + 1] = w[1];
-            }
         }
         for (int i = 0; i < kVB; ++i) {
             const int64_t row = vb * kVB + i;
             const bool live = row < V;
             for (int64_t c = 0; c < G; ++c)
                 o.sr[(vb * G + c) * kVB + i] = live ? sR[row * G + c] : 0;
+            // power-of-two rescale of the row's residual scales for the fp16 path
+            float mx = 0.f;
+            for (int64_t c = 0; live && c < G; ++c)
+                mx = std::max(mx, std::fabs(half_to_float(sR[row * G + c])));
+            const int e = (mx > 0.f && std::isfinite(mx)) ? -std::ilogb(mx) : 0;
+            for (int64_t c = 0; c < G; ++c)
+                o.srp[(vb * G + c) * kVB + i] =
+                    live ? float_to_half(std::ldexp(half_to_float(sR[row * G + c]), e)) : 0;
+            o.rsc[row] = std::ldexp(1.0f, -e);
             o.sa[row] = (live && k > 0) ? sA[row] : 0;
             o.sc[row] = (live && r > 0) ? sC[row] : 0;
         }

@@ -13,7 +13,7 @@ from packed_quantized_lm_amd.synth import make_config, random_small_head, to_bf1
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ["skinny"]
+PATHS = ["skinny", "lds"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -76,6 +76,31 @@ def test_ragged_shapes(shape, path):
     V, d, k, r, g, M = shape
     say(f"ragged {shape} path={path}")
     f = random_small_head(V, d, k, r, g, M, seed=V * 7 + d + M, n_outliers=2, outlier_factor=20.0)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    y, a = gpu_forward(h, f["X"], path=path)
+    assert_logits_close(y, ref, what=str(shape))
+    assert_argmax_ok(a, y, ref, what=str(shape))
+    h.close()
+
+
+# --- several m-tiles and v-ranges of the large-M kernel, ragged in both -------------
+
+LDS_SHAPES = [
+    # V,     d,   k,  r,   g,   M
+    (1500, 512, 64, 16, 128, 300),
+    (600, 256, 16, 4, 32, 257),
+    (1100, 384, 33, 7, 96, 129),
+    (520, 640, 0, 20, 128, 200),
+]
+
+
+@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: "V{}_d{}_k{}_r{}_g{}_M{}".format(*s))
+@pytest.mark.parametrize("path", PATHS)
+def test_multi_tile_shapes(shape, path):
+    V, d, k, r, g, M = shape
+    say(f"multi-tile {shape} path={path}")
+    f = random_small_head(V, d, k, r, g, M, seed=V + d * 3 + M, n_outliers=3, outlier_factor=30.0)
     h = load(f)
     ref = oracle_forward.forward(f, f["X"])
     y, a = gpu_forward(h, f["X"], path=path)
