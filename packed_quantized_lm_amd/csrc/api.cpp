@@ -337,9 +337,12 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
-    HIP_TRY(launch_proj(h->dev, w, Xb, st));
-    if (chosen == ARCHEAD_PATH_LDS)
+    if (chosen == ARCHEAD_PATH_LDS) {
+        HIP_TRY(launch_proj_mfma(h->dev, w, Xb, st));
         HIP_TRY(launch_prep_x16(h->dev, w, Xb, st));
+    } else {
+        HIP_TRY(launch_proj(h->dev, w, Xb, st));
+    }
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
     if (chosen == ARCHEAD_PATH_LDS)

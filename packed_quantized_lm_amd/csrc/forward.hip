@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
     }
 }
 
-hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
+static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
 {
     ProjArgs a;
     a.X = X;
@@ -189,10 +189,152 @@ hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipSt
     a.t16 = w.t16;
     a.s16 = w.s16;
     a.xsneg = w.xsneg;
+    return a;
+}
+
+hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
+{
+    ProjArgs a = proj_args(h, w, X);
     const int64_t ncol = h.s.k + h.s.r;
     a.ncolblk = (int)((ncol + 4 * kProjNI - 1) / (4 * kProjNI));
     dim3 grid(a.ncolblk + 1, (unsigned)((w.M + kProjMB - 1) / kProjMB));
     hipLaunchKernelGGL(proj_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a1 for large M: the same products on the matrix cores.  A workgroup owns 16
+// output columns x 64 hidden states; its 4 waves split d into quarters and
+// their partial sums meet in LDS.  Integer weights enter the MFMA as exact
+// bf16 integers; each g-group of a D8 row is accumulated on its own and
+// folded in with its scale (a group split between two waves is folded by
+// both, which is the same sum).  No per-group X sums: the large-M
+// vocabulary-tile kernel does not use them.
+// ---------------------------------------------------------------------------
+constexpr int kPMB = 4; // 16-row m-blocks per workgroup
+constexpr int kPNB = 4; // K-steps per load batch
+
+// 8 signed int8 values -> 8 exact bf16 integers
+__device__ __forceinline__ u32x4 i8_bf16(u32x2 w)
+{
+    float f[8];
+    for (int e = 0; e < 4; ++e) {
+        f[e] = (float)(int8_t)(w.x >> (8 * e));
+        f[4 + e] = (float)(int8_t)(w.y >> (8 * e));
+    }
+    return u32x4{pack_hi_halves(f[0], f[1]), pack_hi_halves(f[2], f[3]), pack_hi_halves(f[4], f[5]),
+                 pack_hi_halves(f[6], f[7])};
+}
+
+__global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a)
+{
+    __shared__ f32x4 red[4][kPMB][64];
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ncol = a.k + a.r;
+    const int64_t c0 = (int64_t)blockIdx.x * 16;
+    const int64_t c = c0 + lr < ncol ? c0 + lr : ncol - 1;
+    const bool isd = c >= a.k;
+    const int8_t *wrow = (isd ? a.d8 + (c - a.k) * a.d : a.b8 + c * a.d) + 8 * lq;
+    const float *sdrow = a.sd + (isd ? (c - a.k) * a.G : 0);
+    const int64_t mbase = (int64_t)blockIdx.y * (kPMB * 16);
+    const uint16_t *xr[kPMB];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        const int64_t m = mbase + 16 * mb + lr;
+        xr[mb] = a.X + (m < a.M ? m : a.M - 1) * a.d + 8 * lq;
+    }
+    const int64_t nks = a.d / kKStep, gsteps = a.g / kKStep;
+    const int64_t ks0 = wv * (nks / 4), ks1 = ks0 + nks / 4; // d is a multiple of 128
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[kPMB], gacc[kPMB];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+        acc[mb] = gacc[mb] = zero;
+
+    struct Batch {
+        u32x4 x[kPNB][kPMB];
+        u32x2 w[kPNB];
+    };
+    auto load = [&](Batch &b, int64_t ks) {
+#pragma unroll
+        for (int q = 0; q < kPNB; ++q) {
+            const int64_t k = ks + q < ks1 ? ks + q : ks1 - 1;
+#pragma unroll
+            for (int mb = 0; mb < kPMB; ++mb)
+                b.x[q][mb] = *(const u32x4 *)(xr[mb] + k * kKStep);
+            b.w[q] = *(const u32x2 *)(wrow + k * kKStep);
+        }
+    };
+    auto run = [&](const Batch &b, int64_t ks) {
+#pragma unroll
+        for (int q = 0; q < kPNB; ++q) {
+            const int64_t k = ks + q;
+            if (k >= ks1)
+                break;
+            const u32x4 bw = i8_bf16(b.w[q]);
+#pragma unroll
+            for (int mb = 0; mb < kPMB; ++mb)
+                gacc[mb] = mfma_bf16(b.x[q][mb], bw, gacc[mb]);
+            if ((k + 1) % gsteps == 0 || k + 1 == ks1) {
+                const float sc = isd ? sdrow[k / gsteps] : 1.f;
+#pragma unroll
+                for (int mb = 0; mb < kPMB; ++mb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[mb][i] = __builtin_fmaf(sc, gacc[mb][i], acc[mb][i]);
+                    gacc[mb] = zero;
+                }
+            }
+        }
+    };
+    Batch bA, bB;
+    load(bA, ks0);
+    for (int64_t ks = ks0; ks < ks1; ks += 2 * kPNB) {
+        load(bB, ks + kPNB);
+        run(bA, ks);
+        load(bA, ks + 2 * kPNB);
+        run(bB, ks + kPNB);
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb)
+        red[wv][mb][lane] = acc[mb];
+    __syncthreads();
+    if (wv != 0)
+        return;
+    const float sb = isd ? 1.f : a.sb[c];
+#pragma unroll
+    for (int mb = 0; mb < kPMB; ++mb) {
+        const f32x4 v = red[0][mb][lane] + red[1][mb][lane] + red[2][mb][lane] + red[3][mb][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = mbase + 16 * mb + 4 * lq + i;
+            if (m >= a.M || c0 + lr >= ncol)
+                continue;
+            const float t = v[i] * sb;
+            const uint16_t hi = f32_to_bf16_rne(t);
+            const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
+            if (isd) {
+                a.s16[m * a.rpad + (c - a.k)] = hi;
+                a.s16[(a.Mp + m) * a.rpad + (c - a.k)] = lo;
+            } else {
+                a.t16[m * a.kpad + c] = hi;
+                a.t16[(a.Mp + m) * a.kpad + c] = lo;
+            }
+        }
+    }
+}
+
+hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
+{
+    ProjArgs a = proj_args(h, w, X);
+    const int64_t ncol = h.s.k + h.s.r;
+    if (ncol == 0)
+        return hipSuccess;
+    dim3 grid((unsigned)((ncol + 15) / 16), (unsigned)((w.M + kPMB * 16 - 1) / (kPMB * 16)));
+    hipLaunchKernelGGL(proj_mfma_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

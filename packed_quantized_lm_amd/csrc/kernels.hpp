@@ -10,6 +10,10 @@ namespace archead {
 // per-(group, row) X sums the residual kernels need.
 hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 
+// a1 for large M on the matrix cores (t and s only; no per-group X sums, so
+// it pairs with the large-M vocabulary-tile kernel).
+hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
+
 // a2-S: one streaming kernel over vocabulary tiles (any M; the packed codes
 // are streamed once per 32 hidden states): per v-block the low-rank codes,
 // then the SC4 residual, then the logits (if logits is not null) and, if
