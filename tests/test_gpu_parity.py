@@ -291,3 +291,36 @@ def test_prefill_workload_sampled():
         v = a[m]
         assert top[m, idx[v]] >= ref[m].max() - TOL * rms[m]
     say(f"full size {name}: worst sampled |d|/(2e-3 rms) = {ratio:.3g}")
+
+
+# --- HIP graph capture of a step -------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["skinny", "lds"])
+def test_graph_replays_match_eager(path):
+    import torch
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    say(f"graph replay path={path}")
+    f = random_small_head(1500, 512, 64, 16, 128, 40, seed=77)
+    h = load(f)
+    X = x_tensor_from_bits(f["X"])
+    logits = torch.empty((40, 1500), dtype=torch.float32, device="cuda")
+    arg = torch.empty((40,), dtype=torch.int32, device="cuda")
+    h.forward_into(X, logits, arg, path=path)
+    torch.cuda.synchronize()
+    y0, a0 = logits.clone(), arg.clone()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        h.forward_into(X, logits, arg, path=path)
+    for rep in range(4):
+        logits.fill_(float("nan"))
+        arg.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, y0), f"replay {rep}: logits differ"
+        assert torch.equal(arg, a0), f"replay {rep}: argmax differs"
+        h.forward_into(X, logits, arg, path=path)  # eager work between replays
+        torch.cuda.synchronize()
+    del g
+    h.close()
