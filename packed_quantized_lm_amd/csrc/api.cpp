@@ -76,9 +76,7 @@ int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
 
 int64_t max_n_part(const Shape &s)
 {
-    DevHead tmp{};
-    tmp.s = s;
-    return std::max<int64_t>(std::max(skinny_n_part(tmp, 1), lds_n_part(tmp, 1)), 1);
+    return std::max<int64_t>(std::max(skinny_max_n_part(s), lds_max_n_part(s)), 1);
 }
 
 WsLayout ws_layout(const Shape &s, int64_t Mmax)
@@ -140,6 +138,7 @@ Work make_work(archead_t h, int64_t M)
     w.xsc = (float *)(b + L.xsc);
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
+    w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
     return w;
 }
 
@@ -237,6 +236,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     hipStream_t stream = (hipStream_t)hip_stream;
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
     void *block = nullptr;
     hipError_t e = hipMalloc(&block, total);
     if (e != hipSuccess)
@@ -261,6 +262,7 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->dev.r4 = (const uint32_t *)(db + o_r4);
     h->dev.sr = (const uint16_t *)(db + o_sr);
     h->dev.lr = (const uint32_t *)(db + o_lr);
+    h->dev.n_cu = n_cu > 0 ? n_cu : 1;
     h->dev.srp = (const uint16_t *)(db + o_srp);
     h->dev.rsc = (const float *)(db + o_rsc);
     h->dev.sa = (const uint16_t *)(db + o_sa);

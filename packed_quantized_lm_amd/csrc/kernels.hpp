@@ -22,8 +22,10 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
                                int32_t *argmax, hipStream_t st);
 
-// number of argmax partials per row the skinny path writes
+// number of argmax partials per row the skinny path writes for M rows, and
+// the largest such number over every M (sizes the workspace)
 int64_t skinny_n_part(const DevHead &h, int64_t M);
+int64_t skinny_max_n_part(const Shape &s);
 
 // a2-L: LDS-staged MFMA over [128 hidden states x 512 vocabulary rows] tiles
 // for large M.  Needs launch_prep_x16 first (after launch_proj).  The SC4
@@ -34,6 +36,7 @@ hipError_t launch_prep_x16(const DevHead &h, const Work &w, const uint16_t *X, h
 hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int32_t *argmax,
                             hipStream_t st);
 int64_t lds_n_part(const DevHead &h, int64_t M);
+int64_t lds_max_n_part(const Shape &s);
 
 // smallest M for which the automatic choice takes a2-L
 constexpr int64_t kLdsMinM = 128;

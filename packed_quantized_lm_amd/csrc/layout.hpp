@@ -34,8 +34,8 @@
 //       lands the pair's two bits at positions 4 and 20.  Chunks na + j hold
 //       correction K-steps 2j and 2j+1: dwords (0,1) and (2,3) = the lane's 8
 //       columns as offset-binary bytes (c ^ 0x80) in natural order.  The chunk
-//       count n_lr is padded to even; K-steps beyond kst / rst hold the code
-//       of zero and are skipped.
+//       count n_lr is padded to a multiple of 4; K-steps beyond kst / rst hold
+//       the code of zero and are skipped.
 //  srp  uint16 [nvb][G][16]          sR * 2^e_v in fp16 (exact power-of-two
 //       rescale, e_v per row such that the row's largest group scale lies in
 //       [1, 2)); the large-M kernel multiplies residual codes by it in fp16.
@@ -68,10 +68,11 @@ struct Shape {
     __host__ __device__ int64_t rpad() const { return rst() * kKStep; }
     __host__ __device__ int64_t lr_na() const { return (kst() + 2) / 3; }  // A5 chunks
     __host__ __device__ int64_t lr_nc() const { return (rst() + 1) / 2; }  // C8 chunks
-    // total low-rank chunks, rounded up to even so that the residual chunks
-    // start in the first of the two prefetch buffers (the pad chunk is a
-    // correction chunk whose K-steps all lie beyond rst)
-    __host__ __device__ int64_t n_lr() const { return (lr_na() + lr_nc() + 1) / 2 * 2; }
+    // total low-rank chunks, rounded up to a multiple of 4 so that the
+    // residual chunks start in the first of the prefetch buffers in both the
+    // one- and the two-chunk pipelines (pad chunks are correction chunks
+    // whose K-steps all lie beyond rst)
+    __host__ __device__ int64_t n_lr() const { return (lr_na() + lr_nc() + 3) / 4 * 4; }
 
     // element counts of each device array
     __host__ __device__ size_t n_r4() const { return (size_t)nkc() * nvb() * 64 * 4; }      // uint32
@@ -83,6 +84,7 @@ struct Shape {
 // Raw device pointers of one loaded head (all device memory).
 struct DevHead {
     Shape s;
+    int n_cu; // compute units of the device the head lives on
     const uint32_t *r4;
     const uint16_t *sr;
     const uint32_t *lr;
@@ -107,6 +109,7 @@ struct Work {
     float *xsc;        // [Mp][2]  (2^-f_m, 2^f_m)
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;
+    int64_t part_cap;  // uint64 slots in part
 };
 
 // Host relayout (pack.cpp).  Inputs in the canonical host layout; outputs are

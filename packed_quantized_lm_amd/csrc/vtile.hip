@@ -55,8 +55,12 @@ struct Chunk {
 // codes themselves (plus X fragments when X does not fit).  A wave whose
 // v-blocks lie beyond the head streams the last v-block again and stores
 // nothing, so every wave reaches the final barrier.
-template <int NV, int MT, int GS, bool XL, bool TL>
-__global__ __launch_bounds__(256, XL ? 3 : (MT == 1 ? 2 : 1)) void vtile_stream_kernel(StreamArgs a)
+//
+// WIDE (decode: X in LDS, one group per chunk, chunk counts that are
+// multiples of 4): each prefetch buffer holds two K-chunks, so twice the
+// bytes are in flight per v-block, at two waves per SIMD.
+template <int NV, int MT, int GS, bool XL, bool TL, bool WIDE>
+__global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void vtile_stream_kernel(StreamArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MT * 16];
@@ -250,6 +254,61 @@ __global__ __launch_bounds__(256, XL ? 3 : (MT == 1 ? 2 : 1)) void vtile_stream_
         }
     };
 
+    if constexpr (WIDE) {
+        static_assert(XL && GS == 4, "the wide pipeline is for decode shapes");
+        struct Wide {
+            Chunk<NV, MT, XL> h0, h1;
+        };
+        auto load2 = [&](Wide &w, int64_t i) { // stream chunks 2i, 2i + 1
+            load_chunk(w.h0, 2 * i);
+            load_chunk(w.h1, 2 * i + 1);
+        };
+        f32x4 gA[NV][MT], gB[NV][MT];
+        auto mfma_chunk = [&](const Chunk<NV, MT, XL> &c, int64_t kc, f32x4(&g)[NV][MT]) {
+            u32x4 xf[MT][4];
+            x_frags(c, kc, xf);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                kstep(c, s, xf, g, s == 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        Wide wA, wB;
+        load2(wA, 0);
+        load2(wB, 1);
+        __syncthreads(); // LDS staging complete
+        const int64_t nl2 = nlr / 2; // double chunks of low-rank codes (even)
+        for (int64_t i = 0; i < nl2; i += 2) {
+            lr_chunk(wA.h0, 2 * i);
+            lr_chunk(wA.h1, 2 * i + 1);
+            load2(wA, i + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            lr_chunk(wB.h0, 2 * i + 2);
+            lr_chunk(wB.h1, 2 * i + 3);
+            load2(wB, i + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fold_lr();
+        // residual chunk kc: buffer (kc / 2) % 2, half kc % 2, group
+        // accumulator kc % 2, folded one chunk later
+        for (int64_t t = 0; t < nkc / 4; ++t) {
+            const int64_t kc = 4 * t;
+            mfma_chunk(wA.h0, kc, gA);
+            if (t > 0)
+                fold(gB, kc - 1);
+            mfma_chunk(wA.h1, kc + 1, gB);
+            fold(gA, kc);
+            load2(wA, nl2 + 2 * t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_chunk(wB.h0, kc + 2, gA);
+            fold(gB, kc + 1);
+            mfma_chunk(wB.h1, kc + 3, gB);
+            fold(gA, kc + 2);
+            load2(wB, nl2 + 2 * t + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fold(gB, nkc - 1);
+    } else {
     Chunk<NV, MT, XL> bufA, bufB;
     load_chunk(bufA, 0);
     load_chunk(bufB, 1);
@@ -358,6 +417,8 @@ __global__ __launch_bounds__(256, XL ? 3 : (MT == 1 ? 2 : 1)) void vtile_stream_
         }
     }
 
+    } // !WIDE
+
     // logits and the workgroup's top-1 partial keys
     uint64_t key[MT][4];
     for (int mt = 0; mt < MT; ++mt)
@@ -399,14 +460,41 @@ __global__ __launch_bounds__(256, XL ? 3 : (MT == 1 ? 2 : 1)) void vtile_stream_
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-constexpr int kNV = 4;
+constexpr int kNV = 4;   // v-blocks per wave
+constexpr int kNVW = 5;  // v-blocks per wave, wide pipeline (two waves per SIMD)
 constexpr int64_t kXLdsMaxBytes = 48 * 1024;  // X staged in LDS when M*d*2 fits
 constexpr int64_t kTLdsMaxBytes = 64 * 1024;  // t and s staged in LDS when they fit
 
+struct SkinnyPlan {
+    int MT, nv;
+    bool xl, wide;
+};
+
+static SkinnyPlan skinny_plan(const DevHead &h, int64_t M)
+{
+    SkinnyPlan p;
+    p.MT = M <= 16 ? 1 : 2;
+    p.xl = p.MT == 1 && M * h.s.d * 2 <= kXLdsMaxBytes;
+    // the wide pipeline runs two waves per SIMD; it is taken only when all
+    // of its waves are resident at once (a second, partial round of waves
+    // would cost a whole round of time)
+    const int64_t wide_waves = (h.s.nvb() + kNVW - 1) / kNVW;
+    p.wide = p.xl && h.s.g == 4 * kKStep && h.s.nkc() % 4 == 0 && h.s.n_lr() % 4 == 0 &&
+             wide_waves <= int64_t(h.n_cu) * 4 * 2;
+    p.nv = p.wide ? kNVW : kNV;
+    return p;
+}
+
 int64_t skinny_n_part(const DevHead &h, int64_t M)
 {
-    (void)M;
-    return (h.s.nvb() + 4 * kNV - 1) / (4 * kNV);
+    const SkinnyPlan p = skinny_plan(h, M);
+    return (h.s.nvb() + 4 * p.nv - 1) / (4 * p.nv);
+}
+
+int64_t skinny_max_n_part(const Shape &s)
+{
+    const int nv = kNV < kNVW ? kNV : kNVW;
+    return (s.nvb() + 4 * nv - 1) / (4 * nv);
 }
 
 static size_t al16(size_t x) { return (x + 15) / 16 * 16; }
@@ -427,21 +515,24 @@ template <int MT, bool XL, bool TL>
 static hipError_t launch_gs(const StreamArgs &a, dim3 grid, size_t lds, hipStream_t st)
 {
     switch (a.gsteps) {
-    case 4: return launch(vtile_stream_kernel<kNV, MT, 4, XL, TL>, grid, lds, st, a);
-    default: return launch(vtile_stream_kernel<kNV, MT, 0, XL, TL>, grid, lds, st, a);
+    case 4: return launch(vtile_stream_kernel<kNV, MT, 4, XL, TL, false>, grid, lds, st, a);
+    default: return launch(vtile_stream_kernel<kNV, MT, 0, XL, TL, false>, grid, lds, st, a);
     }
 }
 
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
                                int32_t *argmax, hipStream_t st)
 {
-    const int MT = w.M <= 16 ? 1 : 2;
+    const SkinnyPlan p = skinny_plan(h, w.M);
+    const int MT = p.MT;
     const unsigned gy = (unsigned)((w.M + 16 * MT - 1) / (16 * MT));
 
     StreamArgs a;
     a.h = h;
     a.w = w;
     a.w.n_part = skinny_n_part(h, w.M);
+    if (w.M * a.w.n_part > w.part_cap)
+        return hipErrorInvalidValue; // argmax partials would not fit the workspace
     a.X = X;
     a.logits = logits;
     a.want_argmax = argmax ? 1 : 0;
@@ -452,16 +543,19 @@ hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *
     a.nlr = h.s.n_lr();
     a.gsteps = (int)(h.s.g / kKStep);
     a.tl_rows = w.M < 16 * MT ? w.M : 16 * MT;
-    const bool XL = MT == 1 && w.M * h.s.d * 2 <= kXLdsMaxBytes;
+    const bool XL = p.xl;
     const size_t t_bytes = al16(size_t(2) * a.tl_rows * h.s.kpad() * 2);
     const size_t s_bytes = al16(size_t(2) * a.tl_rows * h.s.rpad() * 2);
     const bool TL = t_bytes + s_bytes <= (size_t)kTLdsMaxBytes;
-    a.lds_xs = (unsigned)al16(size_t(4) * kNV * a.G * kVB * 2);
+    a.lds_xs = (unsigned)al16(size_t(4) * p.nv * a.G * kVB * 2);
     a.lds_x = (unsigned)(a.lds_xs + al16(size_t(a.G) * MT * 16 * 4));
     a.lds_t = (unsigned)(a.lds_x + (XL ? al16(size_t(w.M) * h.s.d * 2) : 0));
     a.lds_s = (unsigned)(a.lds_t + (TL ? t_bytes : 0));
     const size_t lds = a.lds_s + (TL ? s_bytes : 0);
     const dim3 grid((unsigned)a.w.n_part, gy);
+    if (p.wide)
+        return TL ? launch(vtile_stream_kernel<kNVW, 1, 4, true, true, true>, grid, lds, st, a)
+                  : launch(vtile_stream_kernel<kNVW, 1, 4, true, false, true>, grid, lds, st, a);
     if (MT == 1) {
         if (XL)
             return TL ? launch_gs<1, true, true>(a, grid, lds, st) : launch_gs<1, true, false>(a, grid, lds, st);

@@ -36,6 +36,7 @@ constexpr int kLW = 8;             // waves per workgroup (two per SIMD)
 constexpr int kLVB = 4;            // v-blocks per wave
 constexpr int kLMB = 8;            // 16-row m-blocks per tile
 constexpr int kLVR = kLW * kLVB;   // v-blocks per workgroup (512 rows)
+constexpr int kLS = 32 / kLW;      // operand blocks each wave fills per stage
 constexpr int kLRows = kLMB * 16;  // hidden states per tile
 // one stage buffer, in 1 KiB blocks (uint32 offsets below)
 constexpr int kLOpBlk = 32;                    // A operand: 32 blocks in lane order
@@ -179,24 +180,24 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     }
 
     // ---- stage fill --------------------------------------------------------
-    // Operand block slot = 4 wv + i (i < 4), m-block slot % 8:
+    // Operand block slot = kLS wv + i (i < kLS), m-block slot % 8:
     //   residual: K-step slot / 8 of the chunk (X rows)
     //   core:     half (slot / 8) % 2 of t (slots 16..31 repeat 0..15)
     //   correction: K-step slot / 16 of the pair, half (slot / 8) % 2 of s
-    // Code block j = 4 wv + i holds the chunk of v-block j of the workgroup.
+    // Code block j = kLVB wv + i holds the chunk of v-block j of the workgroup.
     // Scale block st (residual stages): lane l covers v-block l / 2, rows
     // 8 (l % 2) .. +7, for the group of K-step st (one block when a group
     // spans the whole chunk).
     const uint16_t *x16t = a.w.x16 + mbase * d;
-    const int64_t hsel = (wv >> 1) & 1; // (slot / 8) % 2 for this wave's slots
+    const int64_t hsel = ((wv * kLS) >> 3) & 1; // (slot / 8) % 2 for this wave's slots
     const uint16_t *t16t = a.w.t16 + (hsel * Mp + mbase) * kpad;
     const uint16_t *s16t = a.w.s16 + (hsel * Mp + mbase) * rpad;
     const u32x4 *lrp = (const u32x4 *)a.h.lr;
     const u32x4 *r4p = (const u32x4 *)a.h.r4;
-    const int mb0 = (wv & 1) * 4; // m-block of slot i is mb0 + i
-    uint32_t rowl[4];
+    const int mb0 = (wv * kLS) & 7; // m-block of slot i is mb0 + i
+    uint32_t rowl[kLS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kLS; ++i) {
         const int64_t r = 16 * (mb0 + i) + lr;
         rowl[i] = (uint32_t)(r < rows_live ? r : rows_live - 1);
     }
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         const u32x4 *cbase;
         int64_t kc = 0;
         if (s < p1) {
-            const int64_t ks0 = 2 * s + (wv >> 2), ks = ks0 < rst ? ks0 : rst - 1;
+            const int64_t ks0 = 2 * s + ((wv * kLS) >> 4), ks = ks0 < rst ? ks0 : rst - 1;
             base = s16t + ks * kKStep;
             stride = (uint32_t)rpad;
             cbase = lrp + (a.na + (s < nc ? s : nc - 1)) * nvb * 64;
@@ -221,19 +222,19 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
             cbase = lrp + (ks / 3) * nvb * 64;
         } else {
             kc = s - p2 < nkc ? s - p2 : nkc - 1;
-            base = x16t + (kc * 4 + (wv >> 1)) * kKStep;
+            base = x16t + (kc * 4 + ((wv * kLS) >> 3)) * kKStep;
             stride = (uint32_t)d;
             cbase = r4p + kc * nvb * 64;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_dma16(base + (rowl[i] * stride + 8 * lq), buf + (wv * 4 + i) * 256);
+        for (int i = 0; i < kLS; ++i)
+            lds_dma16(base + (rowl[i] * stride + 8 * lq), buf + (wv * kLS + i) * 256);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kLVB; ++i) {
             const int64_t vb = vb0 + i < nvb ? vb0 + i : nvb - 1;
-            lds_dma16(cbase + vb * 64 + lane, buf + kLCodeOff + (wv * 4 + i) * 256);
+            lds_dma16(cbase + vb * 64 + lane, buf + kLCodeOff + (wv * kLVB + i) * 256);
         }
-        if (s >= p2 && (GS == 4 ? wv == 0 : wv < 4)) {
+        if (s >= p2 && (GS == 4 ? wv == 0 : wv < 4)) { // kLW >= 4
             const int64_t grp = GS == 4 ? kc : (kc * 4 + wv) / gsteps;
             lds_dma16(a.h.srp + (soff + grp * kVB), buf + kLScOff + (GS == 4 ? 0 : wv) * 256);
         }
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     auto codes = [&](const uint32_t *buf, u32x4(&c)[kLVB]) {
 #pragma unroll
         for (int v = 0; v < kLVB; ++v)
-            c[v] = *(const u32x4 *)(buf + kLCodeOff + (wv * 4 + v) * 256 + lane * 4);
+            c[v] = *(const u32x4 *)(buf + kLCodeOff + (wv * kLVB + v) * 256 + lane * 4);
     };
 
     // No branch surrounds an MFMA (the accumulator tile would be copied at
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         for (int v = 0; v < kLVB; ++v)
 #pragma unroll
             for (int st = 0; st < (GS == 4 ? 1 : 4); ++st)
-                sc[v][st] = ((uint32_t)scb[(st * kLVR + wv * 4 + v) * kVB + lr] * 0x10001u) & live;
+                sc[v][st] = ((uint32_t)scb[(st * kLVR + wv * kLVB + v) * kVB + lr] * 0x10001u) & live;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             u32x4 bq[kLVB];
@@ -441,8 +442,10 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 int64_t lds_n_part(const DevHead &h, int64_t M)
 {
     (void)M;
-    return (h.s.nvb() + kLVR - 1) / kLVR;
+    return lds_max_n_part(h.s);
 }
+
+int64_t lds_max_n_part(const Shape &s) { return (s.nvb() + kLVR - 1) / kLVR; }
 
 hipError_t launch_prep_x16(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
 {
@@ -457,6 +460,8 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.h = h;
     a.w = w;
     a.w.n_part = lds_n_part(h, w.M);
+    if (w.M * a.w.n_part > w.part_cap)
+        return hipErrorInvalidValue; // argmax partials would not fit the workspace
     a.logits = logits;
     a.want_argmax = argmax ? 1 : 0;
     a.gsteps = (int)(h.s.g / kKStep);

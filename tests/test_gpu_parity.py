@@ -67,6 +67,8 @@ SHAPES = [
     (777, 512, 40, 0, 512, 33),    # no correction term
     (300, 1024, 256, 64, 128, 64),
     (2500, 256, 16, 4, 32, 1),
+    (3001, 512, 40, 20, 128, 2),   # two-chunk decode pipeline
+    (5000, 1024, 96, 33, 128, 5),  # two-chunk decode pipeline
 ]
 
 
@@ -323,4 +325,19 @@ def test_graph_replays_match_eager(path):
         h.forward_into(X, logits, arg, path=path)  # eager work between replays
         torch.cuda.synchronize()
     del g
+    h.close()
+
+
+def test_argmax_partials_fit_for_every_plan():
+    """The decode plan at M = 1 writes fewer argmax partials per row than the
+    plan at M = 30; a workspace sized for M = 30 must hold the larger count."""
+    say("argmax partials sizing")
+    f = random_small_head(5000, 512, 32, 16, 128, 30, seed=21)
+    h = load(f)
+    h.reserve(30)
+    ref = oracle_forward.forward(f, f["X"])
+    for M in (30, 1, 17):
+        y, a = gpu_forward(h, f["X"][:M])
+        assert_logits_close(y, ref[:M], what=f"M={M}")
+        assert_argmax_ok(a, y, ref[:M], what=f"M={M}")
     h.close()
