@@ -169,6 +169,9 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
     }
 }
 
+constexpr int kPSmallM = 4; // largest M of the one-workgroup-per-column projection
+__global__ void proj_small_kernel(ProjArgs a);
+
 static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
 {
     ProjArgs a;
@@ -196,10 +199,101 @@ hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipSt
 {
     ProjArgs a = proj_args(h, w, X);
     const int64_t ncol = h.s.k + h.s.r;
+    // the X-sum workgroup walks d in windows of 4096 columns, so each
+    // g-group must fall inside one window
+    if (w.M <= kPSmallM && (h.s.d <= 4096 || 4096 % h.s.g == 0)) {
+        hipLaunchKernelGGL(proj_small_kernel, dim3((unsigned)(ncol + 1)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     a.ncolblk = (int)((ncol + 4 * kProjNI - 1) / (4 * kProjNI));
     dim3 grid(a.ncolblk + 1, (unsigned)((w.M + kProjMB - 1) / kProjMB));
     hipLaunchKernelGGL(proj_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a1 for M <= 4 (decode): one workgroup per output column, whose 256 threads
+// cover d in slices of 16 (a single round of loads spread over the chip at
+// d <= 4096), plus one workgroup for the per-group X sums.  Each slice lies
+// inside one g-group, so a D8 row's slice is scaled by its group scale before
+// the workgroup reduction.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void proj_small_kernel(ProjArgs a)
+{
+    __shared__ float red[4][kPSmallM];
+    __shared__ float part[256][kPSmallM];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t ncol = a.k + a.r;
+    const int64_t col = blockIdx.x;
+    const int64_t M = a.M;
+
+    if (col == ncol) { // xsneg[grp][m] = -136 sum_{j in grp} X[m, j]
+        const int64_t per = a.g / 16; // slices per group
+        for (int64_t j00 = 0; j00 < a.d; j00 += 256 * 16) {
+            const int64_t j0 = j00 + 16 * threadIdx.x;
+            for (int m = 0; m < kPSmallM; ++m) {
+                float sum = 0.f;
+                if (j0 < a.d && m < M) {
+                    const u32x4 x0 = *(const u32x4 *)(a.X + m * a.d + j0);
+                    const u32x4 x1 = *(const u32x4 *)(a.X + m * a.d + j0 + 8);
+                    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    for (int e = 0; e < 8; ++e)
+                        sum += bf_lo(xw[e]) + bf_hi(xw[e]);
+                }
+                part[threadIdx.x][m] = sum;
+            }
+            __syncthreads();
+            // groups starting in this 4096-column window
+            const int64_t ngrp = (a.d - j00 < 256 * 16 ? a.d - j00 : 256 * 16) / a.g;
+            if (threadIdx.x < ngrp) {
+                for (int m = 0; m < M; ++m) {
+                    float sum = 0.f;
+                    for (int64_t q = 0; q < per; ++q)
+                        sum += part[threadIdx.x * per + q][m];
+                    a.xsneg[(j00 / a.g + threadIdx.x) * a.Mp + m] = -kR4Bias * sum;
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    const bool isd = col >= a.k;
+    const int8_t *wrow = isd ? a.d8 + (col - a.k) * a.d : a.b8 + col * a.d;
+    float acc[kPSmallM] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t j0 = 16 * threadIdx.x; j0 < a.d; j0 += 256 * 16) {
+        const u32x4 w = *(const u32x4 *)(wrow + j0);
+        const float sc = isd ? a.sd[(col - a.k) * a.G + j0 / a.g] : 1.f;
+        for (int m = 0; m < kPSmallM; ++m) {
+            if (m >= M)
+                break;
+            const u32x4 x0 = *(const u32x4 *)(a.X + m * a.d + j0);
+            const u32x4 x1 = *(const u32x4 *)(a.X + m * a.d + j0 + 8);
+            acc[m] = __builtin_fmaf(sc, dot16(w, x0, x1), acc[m]);
+        }
+    }
+    for (int m = 0; m < kPSmallM; ++m) {
+        float v = acc[m];
+        for (int off = 32; off >= 1; off >>= 1)
+            v += __shfl_xor(v, off);
+        if (lane == 0)
+            red[wv][m] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        const int m = threadIdx.x;
+        const float v = red[0][m] + red[1][m] + red[2][m] + red[3][m];
+        const float t = isd ? v : v * a.sb[col];
+        const uint16_t hi = f32_to_bf16_rne(t);
+        const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
+        if (isd) {
+            a.s16[m * a.rpad + (col - a.k)] = hi;
+            a.s16[(a.Mp + m) * a.rpad + (col - a.k)] = lo;
+        } else {
+            a.t16[m * a.kpad + col] = hi;
+            a.t16[(a.Mp + m) * a.kpad + col] = lo;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -35,7 +35,7 @@ struct StreamArgs {
     int want_argmax;
     int64_t nvb, nkc, G, na, nlr;
     int gsteps;
-    int64_t tl_rows; // rows of t and s staged in LDS per hi/lo half
+    int64_t tl_rows; // most rows of t and s an m-tile stages in LDS per hi/lo half
     unsigned lds_xs, lds_x, lds_t, lds_s; // byte offsets of the LDS regions (sr at 0)
 };
 
@@ -49,8 +49,8 @@ struct Chunk {
 //   sr  [4*NV][G][16]    fp16  residual scales of the workgroup's v-blocks
 //   xs  [G][MT*16]       fp32  -136 x per-group sums of X for the m-tile
 //   x   [M][d]           bf16  the hidden states (XL: small M*d only)
-//   t   [2][tl_rows][kpad] bf16 hi/lo of t for the m-tile's live rows (TL)
-//   s   [2][tl_rows][rpad] bf16 hi/lo of s (TL)
+//   t   [2][rows][kpad]  bf16 hi/lo of t for the m-tile's live rows (TL)
+//   s   [2][rows][rpad]  bf16 hi/lo of s (TL)
 // so that the only vector-memory loads of the streaming loop are the packed
 // codes themselves (plus X fragments when X does not fit).  A wave whose
 // v-blocks lie beyond the head streams the last v-block again and stores
@@ -85,37 +85,42 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
     for (int v = 0; v < NV; ++v)
         vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
 
-    {
+    // LDS staging by direct-to-LDS copies (global_load_lds): every copy of
+    // the workgroup is in flight at once, and the barrier before the
+    // streaming loop waits for all of them (one memory latency in total).
+    // A copy instruction writes its 64 lanes' pieces to consecutive LDS
+    // addresses from a wave-uniform base.
+    auto stage16 = [&](const void *src, void *dst, int64_t n16) { // n16 pieces of 16 bytes
+        for (int64_t i0 = 0; i0 < n16; i0 += 256) {
+            const int64_t i = i0 + threadIdx.x;
+            uint32_t *d0 = (uint32_t *)dst + (i0 + wv * 64) * 4;
+            if (i < n16)
+                __builtin_amdgcn_global_load_lds((const void *)((const u32x4 *)src + i),
+                                                 (__attribute__((address_space(3))) void *)d0, 16, 0, 0);
+        }
+    };
+    auto stage_all = [&]() {
         const int64_t nvb_wg = (nvb - wg_vb0) < 4 * NV ? (nvb - wg_vb0) : 4 * NV;
-        const int64_t n16 = nvb_wg * G * kVB / 8;
-        const u32x4 *src = (const u32x4 *)(a.h.sr + wg_vb0 * G * kVB);
-        for (int64_t i = threadIdx.x; i < n16; i += 256)
-            ((u32x4 *)s_sr)[i] = src[i];
-        for (int64_t i = threadIdx.x; i < G * MT * 16; i += 256) {
+        stage16(a.h.sr + wg_vb0 * G * kVB, s_sr, nvb_wg * G * kVB / 8);
+        // xs[grp][j] = xsneg[grp][mbase + j]: 4-byte pieces, 4 groups per copy
+        for (int64_t i0 = 0; i0 < G * MT * 16; i0 += 256) {
+            const int64_t i = i0 + threadIdx.x;
             const int64_t grp = i / (MT * 16), j = i % (MT * 16);
-            s_xs[i] = a.w.xsneg[grp * Mp + mbase + j];
+            float *d0 = s_xs + i0 + wv * 64;
+            if (i < G * MT * 16)
+                __builtin_amdgcn_global_load_lds((const void *)(a.w.xsneg + grp * Mp + mbase + j),
+                                                 (__attribute__((address_space(3))) void *)d0, 4, 0, 0);
         }
-        if (XL) {
-            const int64_t n16x = M * d / 8;
-            for (int64_t i = threadIdx.x; i < n16x; i += 256)
-                ((u32x4 *)s_x)[i] = ((const u32x4 *)a.X)[i];
-        }
-        if (TL) {
+        if (XL)
+            stage16(a.X, s_x, M * d / 8);
+        if (TL) { // rows mbase .. mbase+rows_live-1 of both halves, hi half first
             const int64_t nt8 = kpad / 8, ns8 = rpad / 8; // 16-byte pieces per row
-            for (int64_t i = threadIdx.x; i < 2 * rows_live * nt8; i += 256) {
-                const int64_t h = i / (rows_live * nt8), rem = i % (rows_live * nt8);
-                const int64_t rr = rem / nt8, c = rem % nt8;
-                ((u32x4 *)s_t)[(h * a.tl_rows + rr) * nt8 + c] =
-                    *(const u32x4 *)(a.w.t16 + (h * Mp + mbase + rr) * kpad + c * 8);
-            }
-            for (int64_t i = threadIdx.x; i < 2 * rows_live * ns8; i += 256) {
-                const int64_t h = i / (rows_live * ns8), rem = i % (rows_live * ns8);
-                const int64_t rr = rem / ns8, c = rem % ns8;
-                ((u32x4 *)s_s)[(h * a.tl_rows + rr) * ns8 + c] =
-                    *(const u32x4 *)(a.w.s16 + (h * Mp + mbase + rr) * rpad + c * 8);
+            for (int h = 0; h < 2; ++h) {
+                stage16(a.w.t16 + (h * Mp + mbase) * kpad, s_t + h * rows_live * kpad, rows_live * nt8);
+                stage16(a.w.s16 + (h * Mp + mbase) * rpad, s_s + h * rows_live * rpad, rows_live * ns8);
             }
         }
-    }
+    };
 
     // Rows m >= M of the A operand only feed output rows that are never
     // stored, so they read the last live row instead of branching around the
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
     const uint16_t *xl = s_x + (lr < M ? lr : M - 1) * d + 8 * lq; // XL: MT == 1, mbase == 0
     const uint16_t *tb = TL ? s_t : a.w.t16 + mbase * kpad;
     const uint16_t *sb = TL ? s_s : a.w.s16 + mbase * rpad;
-    const int64_t hst = TL ? a.tl_rows : Mp; // rows between the hi and lo halves
+    const int64_t hst = TL ? rows_live : Mp; // rows between the hi and lo halves
     int64_t trow[MT];
     for (int mt = 0; mt < MT; ++mt)
         trow[mt] = (mt * 16 + lr) < rows_live ? (mt * 16 + lr) : rows_live - 1;
@@ -276,6 +281,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
         Wide wA, wB;
         load2(wA, 0);
         load2(wB, 1);
+        stage_all();
         __syncthreads(); // LDS staging complete
         const int64_t nl2 = nlr / 2; // double chunks of low-rank codes (even)
         for (int64_t i = 0; i < nl2; i += 2) {
@@ -312,6 +318,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
     Chunk<NV, MT, XL> bufA, bufB;
     load_chunk(bufA, 0);
     load_chunk(bufB, 1);
+    stage_all();
     __syncthreads(); // LDS staging complete
 
     // low-rank chunks (nlr is even): bufA holds chunk c, bufB chunk c + 1
