@@ -69,10 +69,11 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, x16, xsc, part, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
+int64_t round_m128(int64_t M) { return (M + 127) / 128 * 128; }
 
 int64_t max_n_part(const Shape &s)
 {
@@ -90,10 +91,19 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(2) * Mp * s.rpad() * 2);
     L.xsneg = off;
     off = align_up(off + size_t(s.G()) * Mp * 4);
-    L.x16 = off;
-    off = align_up(off + size_t(Mp) * s.d * 2);
+    const int64_t Mq = round_m128(std::max<int64_t>(Mmax, 1));
+    L.tf32 = off;
+    off = align_up(off + size_t(Mp) * s.kpad() * 4);
+    L.sf32 = off;
+    off = align_up(off + size_t(Mp) * s.rpad() * 4);
+    L.xsw = off;
+    off = align_up(off + size_t(Mq) * s.d * 2);
+    L.tsw = off;
+    off = align_up(off + size_t(2) * Mq * s.kpad() * 2);
+    L.ssw = off;
+    off = align_up(off + size_t(2) * Mq * s.rpad() * 2);
     L.xsc = off;
-    off = align_up(off + size_t(Mp) * 2 * 4);
+    off = align_up(off + size_t(Mq) * 2 * 4);
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
     L.total = off;
@@ -134,8 +144,13 @@ Work make_work(archead_t h, int64_t M)
     w.t16 = (uint16_t *)(b + L.t16);
     w.s16 = (uint16_t *)(b + L.s16);
     w.xsneg = (float *)(b + L.xsneg);
-    w.x16 = (uint16_t *)(b + L.x16);
+    w.tf32 = (float *)(b + L.tf32);
+    w.sf32 = (float *)(b + L.sf32);
+    w.xsw = (uint16_t *)(b + L.xsw);
+    w.tsw = (uint16_t *)(b + L.tsw);
+    w.ssw = (uint16_t *)(b + L.ssw);
     w.xsc = (float *)(b + L.xsc);
+    w.Mq = round_m128(std::max<int64_t>(h->ws_M, 1));
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
     w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
@@ -209,6 +224,7 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     };
     const size_t o_r4 = place(s.n_r4() * 4), o_sr = place(s.n_sr() * 2);
     const size_t o_srp = place(s.n_sr() * 2), o_rsc = place(s.n_rows() * 4);
+    const size_t o_sap = place(s.n_rows() * 2), o_scp = place(s.n_rows() * 2);
     const size_t o_lr = place(s.n_lr_words() * 4);
     const size_t o_sa = place(s.n_rows() * 2);
     const size_t o_sc = place(s.n_rows() * 2), o_b8 = place(size_t(k) * d);
@@ -224,7 +240,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     }
     char *hb = host.data();
     HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_lr),
-                     (uint16_t *)(hb + o_srp), (float *)(hb + o_rsc), (uint16_t *)(hb + o_sa),
+                     (uint16_t *)(hb + o_srp), (uint16_t *)(hb + o_sap), (uint16_t *)(hb + o_scp),
+                     (float *)(hb + o_rsc), (uint16_t *)(hb + o_sa),
                      (uint16_t *)(hb + o_sc), (float *)(hb + o_sb), (float *)(hb + o_sd)};
     relayout(s, A5, sA, sB, R4, sR, C8, sC, sD, img,
              (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency())));
@@ -265,6 +282,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->dev.n_cu = n_cu > 0 ? n_cu : 1;
     h->dev.srp = (const uint16_t *)(db + o_srp);
     h->dev.rsc = (const float *)(db + o_rsc);
+    h->dev.sap = (const uint16_t *)(db + o_sap);
+    h->dev.scp = (const uint16_t *)(db + o_scp);
     h->dev.sa = (const uint16_t *)(db + o_sa);
     h->dev.sc = (const uint16_t *)(db + o_sc);
     h->dev.b8 = (const int8_t *)(db + o_b8);
@@ -341,7 +360,7 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     const uint16_t *Xb = (const uint16_t *)X;
     if (chosen == ARCHEAD_PATH_LDS) {
         HIP_TRY(launch_proj_mfma(h->dev, w, Xb, st));
-        HIP_TRY(launch_prep_x16(h->dev, w, Xb, st));
+        HIP_TRY(launch_prep_lds(h->dev, w, Xb, st));
     } else {
         HIP_TRY(launch_proj(h->dev, w, Xb, st));
     }

@@ -33,6 +33,7 @@ struct ProjArgs {
     const int8_t *d8;
     const float *sd;
     uint16_t *t16, *s16;
+    float *tf32, *sf32; // fp32 t and s (large-M projection)
     float *xsneg;
     int ncolblk;
 };
@@ -191,6 +192,8 @@ static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
     a.sd = h.sd;
     a.t16 = w.t16;
     a.s16 = w.s16;
+    a.tf32 = w.tf32;
+    a.sf32 = w.sf32;
     a.xsneg = w.xsneg;
     return a;
 }
@@ -297,9 +300,10 @@ __global__ __launch_bounds__(256) void proj_small_kernel(ProjArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// a1 for large M: the same products on the matrix cores.  A workgroup owns 16
-// output columns x 64 hidden states; its 4 waves split d into quarters and
-// their partial sums meet in LDS.  Integer weights enter the MFMA as exact
+// a1 for large M: the same products on the matrix cores, written as fp32 t
+// and s for the large-M vocabulary-tile path.  A workgroup owns 16 output
+// columns x 64 hidden states; its 4 waves split d into quarters and their
+// partial sums meet in LDS.  Integer weights enter the MFMA as exact
 // bf16 integers; each g-group of a D8 row is accumulated on its own and
 // folded in with its scale (a group split between two waves is folded by
 // both, which is the same sum).  No per-group X sums: the large-M
@@ -407,16 +411,10 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a)
             const int64_t m = mbase + 16 * mb + 4 * lq + i;
             if (m >= a.M || c0 + lr >= ncol)
                 continue;
-            const float t = v[i] * sb;
-            const uint16_t hi = f32_to_bf16_rne(t);
-            const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
-            if (isd) {
-                a.s16[m * a.rpad + (c - a.k)] = hi;
-                a.s16[(a.Mp + m) * a.rpad + (c - a.k)] = lo;
-            } else {
-                a.t16[m * a.kpad + c] = hi;
-                a.t16[(a.Mp + m) * a.kpad + c] = lo;
-            }
+            if (isd)
+                a.sf32[m * a.rpad + (c - a.k)] = v[i];
+            else
+                a.tf32[m * a.kpad + c] = v[i] * sb;
         }
     }
 }

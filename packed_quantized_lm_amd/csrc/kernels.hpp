@@ -10,8 +10,8 @@ namespace archead {
 // per-(group, row) X sums the residual kernels need.
 hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 
-// a1 for large M on the matrix cores (t and s only; no per-group X sums, so
-// it pairs with the large-M vocabulary-tile kernel).
+// a1 for large M on the matrix cores: fp32 t and s into w.tf32 / w.sf32 (no
+// per-group X sums); it pairs with the large-M vocabulary-tile kernel.
 hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 
 // a2-S: one streaming kernel over vocabulary tiles (any M; the packed codes
@@ -27,12 +27,12 @@ hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *
 int64_t skinny_n_part(const DevHead &h, int64_t M);
 int64_t skinny_max_n_part(const Shape &s);
 
-// a2-L: LDS-staged MFMA over [128 hidden states x 512 vocabulary rows] tiles
-// for large M.  Needs launch_prep_x16 first (after launch_proj).  The SC4
-// term is computed in fp16 MFMA with sR * R4 rounded once to fp16; the
-// low-rank terms use exact integer bf16 codes against the hi/lo parts of t
-// and s.  Argmax partials as for a2-S.
-hipError_t launch_prep_x16(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
+// a2-L: LDS-staged fp16 MFMA over [128 hidden states x 512 vocabulary rows]
+// tiles for large M.  Needs launch_proj_mfma then launch_prep_lds first.
+// Every B operand is an integer code times its row-normalised scale, rounded
+// once to fp16; the A operands are X, and the fp16 hi/lo parts of t and s,
+// scaled by a per-row power of two.  Argmax partials as for a2-S.
+hipError_t launch_prep_lds(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st);
 hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int32_t *argmax,
                             hipStream_t st);
 int64_t lds_n_part(const DevHead &h, int64_t M);

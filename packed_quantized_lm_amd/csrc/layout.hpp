@@ -36,9 +36,11 @@
 //       columns as offset-binary bytes (c ^ 0x80) in natural order.  The chunk
 //       count n_lr is padded to a multiple of 4; K-steps beyond kst / rst hold
 //       the code of zero and are skipped.
-//  srp  uint16 [nvb][G][16]          sR * 2^e_v in fp16 (exact power-of-two
-//       rescale, e_v per row such that the row's largest group scale lies in
-//       [1, 2)); the large-M kernel multiplies residual codes by it in fp16.
+//  srp  uint16 [nvb][G][16]          sR * 2^e_v in fp16, an exact power-of-two
+//       rescale with e_v per row such that the row's largest scale (over its
+//       sR groups, sA and sC) lies in [1, 2); the large-M kernel multiplies
+//       the codes by these in fp16.
+//  sap, scp uint16 [nvb*16]          sA * 2^e_v and sC * 2^e_v in fp16.
 //  rsc  float  [nvb*16]              2^-e_v per row.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
@@ -89,6 +91,8 @@ struct DevHead {
     const uint16_t *sr;
     const uint32_t *lr;
     const uint16_t *srp;
+    const uint16_t *sap;
+    const uint16_t *scp;
     const float *rsc;
     const uint16_t *sa;
     const uint16_t *sc;
@@ -105,8 +109,14 @@ struct Work {
     uint16_t *t16;     // [2][Mp][kpad] bf16 hi/lo of t = X (sB o B8)^T
     uint16_t *s16;     // [2][Mp][rpad] bf16 hi/lo of s = X (sD o D8)^T
     float *xsneg;      // [G][Mp]  -136 * sum_{j in group} X[m, j]
-    uint16_t *x16;     // [Mp][d]  fp16 of X[m, :] * 2^f_m (large-M path)
-    float *xsc;        // [Mp][2]  (2^-f_m, 2^f_m)
+    // large-M path (Mq = M rounded up to 128):
+    float *tf32;       // [Mp][kpad] t in fp32
+    float *sf32;       // [Mp][rpad] s in fp32
+    uint16_t *xsw;     // [Mq/16][d/32][64][8]    fp16 X 2^f_m in MFMA A-operand blocks
+    uint16_t *tsw;     // [Mq/16][kst][2][64][8]  fp16 hi/lo of t 2^f_m, same blocks
+    uint16_t *ssw;     // [Mq/16][rst][2][64][8]  fp16 hi/lo of s 2^f_m
+    float *xsc;        // [Mq][2]  (2^-f_m, 2^f_m)
+    int64_t Mq;
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;
     int64_t part_cap;  // uint64 slots in part
@@ -119,6 +129,8 @@ struct HostDevImage {
     uint16_t *sr;
     uint32_t *lr;
     uint16_t *srp;
+    uint16_t *sap;
+    uint16_t *scp;
     float *rsc;
     uint16_t *sa;
     uint16_t *sc;

@@ -1,5 +1,5 @@
 // vtile_lds.hip -- the vocabulary-tile step of the packed ARCHead forward for
-// large M (prefill): LDS-staged MFMA over [128 hidden states x 512 rows].
+// large M (prefill): LDS-staged fp16 MFMA over [128 hidden states x 512 rows].
 //
 // ARCHead paper, section 3.2, eq 7, with W_d of eq 3 and the INT8 correction
 // factors stored after eq 7:
@@ -8,19 +8,24 @@
 // At large M the step is bound by the matrix cores, not by HBM.  A workgroup
 // of 8 waves owns 128 hidden states x 32 v-blocks; each wave keeps a
 // [128 x 64] fp32 accumulator tile.  Everything a stage needs -- the A
-// operand (X, t or s for the 128 rows), the code chunks of the 32 v-blocks
-// and their residual scales -- is copied straight from global memory into
-// LDS (global_load_lds), double-buffered with one barrier per stage.
+// operand blocks for the 128 rows, the code words of the 32 v-blocks and
+// their residual scales -- is copied straight from global memory into LDS
+// (global_load_lds), double-buffered with one barrier per stage.
 //
-// Precision (one accumulator per output, three phases):
-//   1. correction: exact integer C8 codes (bf16) against s = s_hi + s_lo;
-//   2. rescale by sC/sA, then the core: exact integer A5 codes against
-//      t = t_hi + t_lo; rows whose sA or sC is zero have those codes masked;
-//   3. rescale by sA 2^e_v 2^f_m, then the residual in fp16 MFMA: the code q
-//      times the row-normalised scale sR 2^e_v, rounded once to fp16
-//      (relative error <= 2^-12), against X 2^f_m converted to fp16 (exact
-//      for every element within 2^29 of the row maximum);
-// then the powers of two are removed.  Every other step is exact or fp32.
+// One accumulator and one MFMA type (v_mfma_f32_16x16x32_f16) for all three
+// terms, in three phases.  With e_v the row's scale exponent (layout.hpp)
+// and f_m a per-hidden-state power of two (prep_lds_kernel):
+//   1. residual: B = q x (sR 2^e_v), rounded once to fp16 (relative error at
+//      most 2^-12 of this, the smallest, term; q and the power-of-two rescale
+//      are exact), A = X 2^f_m in fp16 (exact for every element within 2^29
+//      of the row's largest operand);
+//   2. rescale the accumulator (fp32) to units of sC[v] 2^-f_m; correction:
+//      B = the exact integer codes C8, A = the fp16 hi + lo parts of
+//      s 2^f_m (22 significant bits);
+//   3. rescale to units of sA[v] 2^-f_m; core: B = the exact integer codes
+//      A5, A = hi + lo of t 2^f_m;
+// and the epilogue multiplies by sA[v] 2^-f_m.  Rows whose sC (sA) is zero
+// have their C8 (A5) codes masked and keep a unit divisor.
 //
 // Tiles are assigned so that the workgroups one XCD runs share v-ranges: the
 // 16 m-tiles of a v-range run on the same XCD at about the same time, so its
@@ -36,33 +41,52 @@ constexpr int kLW = 8;             // waves per workgroup (two per SIMD)
 constexpr int kLVB = 4;            // v-blocks per wave
 constexpr int kLMB = 8;            // 16-row m-blocks per tile
 constexpr int kLVR = kLW * kLVB;   // v-blocks per workgroup (512 rows)
-constexpr int kLS = 32 / kLW;      // operand blocks each wave fills per stage
+constexpr int kLS = 32 / kLW;      // operand blocks each wave copies per stage
 constexpr int kLRows = kLMB * 16;  // hidden states per tile
-// one stage buffer, in 1 KiB blocks (uint32 offsets below)
-constexpr int kLOpBlk = 32;                    // A operand: 32 blocks in lane order
-constexpr int kLCodeOff = kLOpBlk * 256;       // code chunks of the 32 v-blocks
-constexpr int kLScOff = kLCodeOff + kLVR * 256; // residual scales [4 K-steps][32 v-blocks][16] fp16
-constexpr int kLStageWords = kLScOff + 4 * 256;
+// one stage buffer (uint32 offsets)
+constexpr int kLCodeOff = 32 * 256;                  // 32 operand blocks of 1 KiB
+constexpr int kLScOff = kLCodeOff + kLVR * 256;      // code words, 1 KiB per v-block
+constexpr int kLStageWords = kLScOff + 4 * kLVR * 8; // residual scales [4 K-steps][32][16] fp16
 
 // ---------------------------------------------------------------------------
-// X -> fp16 with a per-row power-of-two scale (max |X[m,:]| 2^f in
-// [2^14, 2^15)); bf16 values convert exactly unless 2^29 below the maximum.
+// Operand preparation: per hidden state m, f_m puts the largest of |X[m,:]|,
+// |t[m,:]|, |s[m,:]| into [2^14, 2^15); X 2^f_m (fp16) and the fp16 hi/lo
+// parts of t 2^f_m and s 2^f_m are written in MFMA A-operand blocks of
+// [16 rows x 32 columns] (lane l: row l % 16, columns 8 (l / 16) .. +7), so
+// that each block is one contiguous 1 KiB copy.  Rows M .. (tile end) are
+// zeros.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prep_x16_kernel(const uint16_t *X, int64_t d, uint16_t *x16,
-                                                       float *xsc)
+struct PrepArgs {
+    const uint16_t *X;
+    const float *tf32, *sf32;
+    int64_t M, d, k, r, kst, rst, kpad, rpad;
+    uint16_t *xsw, *tsw, *ssw;
+    float *xsc;
+};
+
+__device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__global__ __launch_bounds__(256) void prep_lds_kernel(PrepArgs a)
 {
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
-    const uint16_t *xr = X + m * d;
+    const bool live = m < a.M;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     float mx = 0.f;
-    for (int64_t j = threadIdx.x * 8; j < d; j += 256 * 8) {
-        const u32x4 v = *(const u32x4 *)(xr + j);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        for (int q = 0; q < 4; ++q) {
-            mx = fmaxf(mx, fabsf(__uint_as_float(w[q] << 16)));
-            mx = fmaxf(mx, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+    if (live) {
+        const uint16_t *xr = a.X + m * a.d;
+        for (int64_t j = threadIdx.x * 8; j < a.d; j += 256 * 8) {
+            const u32x4 v = *(const u32x4 *)(xr + j);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 4; ++q) {
+                mx = fmaxf(mx, fabsf(__uint_as_float(w[q] << 16)));
+                mx = fmaxf(mx, fabsf(__uint_as_float(w[q] & 0xFFFF0000u)));
+            }
         }
+        for (int64_t c = threadIdx.x; c < a.k; c += 256)
+            mx = fmaxf(mx, fabsf(a.tf32[m * a.kpad + c]));
+        for (int64_t c = threadIdx.x; c < a.r; c += 256)
+            mx = fmaxf(mx, fabsf(a.sf32[m * a.rpad + c]));
     }
     for (int off = 32; off >= 1; off >>= 1)
         mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -75,45 +99,103 @@ __global__ __launch_bounds__(256) void prep_x16_kernel(const uint16_t *X, int64_
         f = 14 - ilogbf(mx);
         f = f < -126 ? -126 : (f > 126 ? 126 : f);
     }
-    for (int64_t j = threadIdx.x * 8; j < d; j += 256 * 8) {
-        const u32x4 v = *(const u32x4 *)(xr + j);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[4];
-        for (int q = 0; q < 4; ++q) {
-            const _Float16 lo = (_Float16)ldexpf(__uint_as_float(w[q] << 16), f);
-            const _Float16 hi = (_Float16)ldexpf(__uint_as_float(w[q] & 0xFFFF0000u), f);
-            o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        *(u32x4 *)(x16 + m * d + j) = u32x4{o[0], o[1], o[2], o[3]};
-    }
     if (threadIdx.x == 0) {
-        xsc[2 * m] = ldexpf(1.f, -f);
-        xsc[2 * m + 1] = ldexpf(1.f, f);
+        a.xsc[2 * m] = ldexpf(1.f, -f);
+        a.xsc[2 * m + 1] = ldexpf(1.f, f);
     }
+    const int64_t mb16 = m >> 4, lrow = m & 15, nks = a.d / kKStep;
+    // X: piece p = (K-step p / 4, quarter p % 4)
+    for (int64_t p = threadIdx.x; p < a.d / 8; p += 256) {
+        const int64_t ks = p >> 2, qq = p & 3;
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+        if (live) {
+            const u32x4 v = *(const u32x4 *)(a.X + m * a.d + 8 * p);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 4; ++q)
+                o[q] = (uint32_t)f16_bits(ldexpf(__uint_as_float(w[q] << 16), f)) |
+                       ((uint32_t)f16_bits(ldexpf(__uint_as_float(w[q] & 0xFFFF0000u), f)) << 16);
+        }
+        *(u32x4 *)(a.xsw + ((mb16 * nks + ks) * 64 + lrow + 16 * qq) * 8) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    // t and s: hi and lo parts in consecutive blocks
+    auto hilo = [&](const float *src, int64_t ncol, int64_t pitch, int64_t nst, uint16_t *dst) {
+        for (int64_t p = threadIdx.x; p < nst * 4; p += 256) {
+            const int64_t ks = p >> 2, qq = p & 3;
+            uint16_t hi[8], lo[8];
+            for (int e = 0; e < 8; ++e) {
+                const int64_t c = 8 * p + e;
+                const float v = (live && c < ncol) ? ldexpf(src[m * pitch + c], f) : 0.f;
+                const _Float16 h = (_Float16)v;
+                hi[e] = __builtin_bit_cast(uint16_t, h);
+                lo[e] = f16_bits(v - (float)h);
+            }
+            uint32_t oh[4], ol[4];
+            for (int q = 0; q < 4; ++q) {
+                oh[q] = (uint32_t)hi[2 * q] | ((uint32_t)hi[2 * q + 1] << 16);
+                ol[q] = (uint32_t)lo[2 * q] | ((uint32_t)lo[2 * q + 1] << 16);
+            }
+            const int64_t blk = (mb16 * nst + ks) * 2;
+            *(u32x4 *)(dst + ((blk + 0) * 64 + lrow + 16 * qq) * 8) = u32x4{oh[0], oh[1], oh[2], oh[3]};
+            *(u32x4 *)(dst + ((blk + 1) * 64 + lrow + 16 * qq) * 8) = u32x4{ol[0], ol[1], ol[2], ol[3]};
+        }
+    };
+    hilo(a.tf32, a.k, a.kpad, a.kst, a.tsw);
+    hilo(a.sf32, a.r, a.rpad, a.rst, a.ssw);
 }
 
-// bf16 pair of exact integers (a + 144) -> bf16 pair a
-__device__ __forceinline__ uint32_t unbias144(uint32_t p)
+// ---------------------------------------------------------------------------
+// B-operand dequantisation: integer codes -> exact fp16 integers (exponent
+// splicing: 0x6400 | u = 1024 + u for u < 1024, then one exact subtraction)
+// -> times the row's fp16 scale, rounded once.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f16x2_code_times(uint32_t spliced, float bias, f16x2 s2)
 {
-    const float lo = __uint_as_float(p << 16) - kA5Bias;
-    const float hi = __uint_as_float(p & 0xFFFF0000u) - kA5Bias;
-    return pack_hi_halves(lo, hi);
+    const f16x2 b = {(_Float16)bias, (_Float16)bias};
+    f16x2 h = __builtin_bit_cast(f16x2, spliced) - b; // exact: the signed code
+    h = h * s2;                                       // rounded once
+    return __builtin_bit_cast(uint32_t, h);
 }
 
-// residual dword -> 8 fp16 values q * s (q = nibble - 8), s2 = (s, s)
-__device__ __forceinline__ u32x4 r4_f16_scaled(uint32_t w, uint32_t magic, f16x2 s2)
+// residual dword (8 offset-binary nibbles, slot order of layout.hpp)
+__device__ __forceinline__ u32x4 r4_f16(uint32_t w, uint32_t magic, f16x2 s2)
 {
-    const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
     const uint32_t m = 0x000F000Fu;
-    const uint32_t x[4] = {(w & m) | magic, ((w >> 4) & m) | magic, ((w >> 8) & m) | magic,
-                           ((w >> 12) & m) | magic};
+    return u32x4{f16x2_code_times((w & m) | magic, 1032.f, s2),
+                 f16x2_code_times(((w >> 4) & m) | magic, 1032.f, s2),
+                 f16x2_code_times(((w >> 8) & m) | magic, 1032.f, s2),
+                 f16x2_code_times(((w >> 12) & m) | magic, 1032.f, s2)};
+}
+
+// exact fp16 integers from spliced codes: (1024 + u) - bias
+__device__ __forceinline__ uint32_t f16x2_code(uint32_t spliced, float bias)
+{
+    const f16x2 b = {(_Float16)bias, (_Float16)bias};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, spliced) - b);
+}
+
+// 5-bit core codes of one K-step as exact fp16 integers: nibble dword +
+// high-bit dword (the K-step is number qq of its chunk)
+__device__ __forceinline__ u32x4 a5_f16(uint32_t wn, uint32_t wh, int qq, uint32_t magic)
+{
+    const uint32_t m = 0x000F000Fu, hb = 0x00100010u;
     uint32_t o[4];
     for (int p = 0; p < 4; ++p) {
-        f16x2 h = __builtin_bit_cast(f16x2, x[p]) - bias; // exact: q
-        h = h * s2;                                       // rounded once
-        o[p] = __builtin_bit_cast(uint32_t, h);
+        const uint32_t u = ((wn >> (4 * p)) & m) | (rotr(wh, 4 * qq + p) & hb) | magic;
+        o[p] = f16x2_code(u, 1040.f); // (1024 + a + 16) - 1040 = a
     }
     return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// correction codes of one K-step (two dwords of offset-binary bytes c ^ 0x80)
+// as exact fp16 integers
+__device__ __forceinline__ u32x4 c8_f16(uint32_t w0, uint32_t w1, uint32_t magic)
+{
+    // bytes 2p, 2p+1 of a dword into the low bytes of its two 16-bit halves
+    // (v_perm_b32: selector 0x0c gives a zero byte)
+    const uint32_t p0 = __builtin_amdgcn_perm(0u, w0, 0x0c010c00u), p1 = __builtin_amdgcn_perm(0u, w0, 0x0c030c02u);
+    const uint32_t p2 = __builtin_amdgcn_perm(0u, w1, 0x0c010c00u), p3 = __builtin_amdgcn_perm(0u, w1, 0x0c030c02u);
+    return u32x4{f16x2_code(p0 | magic, 1152.f), f16x2_code(p1 | magic, 1152.f), f16x2_code(p2 | magic, 1152.f),
+                 f16x2_code(p3 | magic, 1152.f)}; // (1024 + c + 128) - 1152 = c
 }
 
 __device__ __forceinline__ u32x4 and4(u32x4 v, uint32_t m) { return u32x4{v.x & m, v.y & m, v.z & m, v.w & m}; }
@@ -124,19 +206,29 @@ struct LdsArgs {
     float *logits; // may be null
     int want_argmax;
     int gsteps;
-    int64_t nvb, nkc, G, na, nc, kst, rst, kpad, rpad;
-    int64_t p1, p2, nst; // first core stage, first residual stage, stage count (phases padded to even)
+    int64_t nvb, nkc, G, na, nc, kst, rst;
+    int64_t nsr, nsc, nsa; // residual / correction / core stages, each padded to even
     int64_t n_vr, n_mt, n_tiles, per_xcd;
 };
 
+// direct copies into LDS: lane l's piece lands at dst + l pieces
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t *dst)
 {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
 }
+__device__ __forceinline__ void lds_dma4(const void *src, uint32_t *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+}
 
-// Stages, in order: correction stages (two K-steps of s_hi/s_lo each), core
-// stages (one K-step of t_hi/t_lo), residual stages (four K-steps of X), each
-// phase padded to an even count; a pad stage contributes zero.
+// Stages, in order: nsc correction stages (K-steps 2j, 2j+1 of s), nsa core
+// stages (K-steps 2j, 2j+1 of t), nkc residual stages (the four K-steps of
+// K-chunk kc of X), then one pad stage when the count is odd.  Each stage
+// has four operand slots q, each with 8 A blocks (one per m-block) and one B
+// operand per v-block: correction and core slot q = 2 hh + half takes the hi
+// or lo part of K-step 2j + hh; residual slot q is K-step q.  Every stage
+// runs the same 128 MFMAs per wave; slots past the end of a phase, and the
+// pad stage, have their B operands masked to zero.
 template <int GS>
 __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 {
@@ -156,87 +248,99 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     if (L >= a.n_tiles)
         return; // the whole workgroup
     const int64_t vr = L / a.n_mt, mt = L % a.n_mt;
-    const int64_t M = a.w.M, Mp = a.w.Mp, d = a.h.s.d, V = a.h.s.V;
-    const int64_t nvb = a.nvb, G = a.G, nc = a.nc, kst = a.kst, rst = a.rst, nkc = a.nkc;
-    const int64_t kpad = a.kpad, rpad = a.rpad, nst = a.nst, p1 = a.p1, p2 = a.p2;
-    const int64_t mbase = mt * kLRows;
-    const int64_t rows_live = (M - mbase) < kLRows ? (M - mbase) : kLRows;
+    const int64_t M = a.w.M, d = a.h.s.d, V = a.h.s.V;
+    const int64_t nvb = a.nvb, G = a.G, nkc = a.nkc, kst = a.kst, rst = a.rst;
+    // stage ranges: residual [0, p1), correction [p1, p2), core [p2, nst)
+    const int64_t p1 = a.nsr, p2 = a.nsr + a.nsc, nst = a.nsr + a.nsc + a.nsa;
+    const int64_t mbase = mt * kLRows, mb16_0 = mt * kLMB;
     const int64_t wg_vb0 = vr * kLVR;
     const int64_t vb0 = wg_vb0 + wv * kLVB;
+    const int64_t nks = d / kKStep;
     const int gsteps = GS ? GS : a.gsteps;
 
+    int64_t vb[kLVB];
     // bit v: sA of the lane's row in v-block v is nonzero; bit kLVB + v: sC
     uint32_t nz = 0;
 #pragma unroll
     for (int v = 0; v < kLVB; ++v) {
-        const int64_t vb = vb0 + v < nvb ? vb0 + v : nvb - 1;
-        nz |= h2f(a.h.sa[vb * kVB + lr]) != 0.f ? 1u << v : 0u;
-        nz |= h2f(a.h.sc[vb * kVB + lr]) != 0.f ? 1u << (kLVB + v) : 0u;
+        vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
+        nz |= h2f(a.h.sa[vb[v] * kVB + lr]) != 0.f ? 1u << v : 0u;
+        nz |= h2f(a.h.sc[vb[v] * kVB + lr]) != 0.f ? 1u << (kLVB + v) : 0u;
     }
+    // unit divisors: sA (sC) of the lane's row, or 1 where it is zero
+    auto pa = [&](int v) { const float x = h2f(a.h.sa[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
+    auto pc = [&](int v) { const float x = h2f(a.h.sc[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
     if (threadIdx.x < kLRows) {
-        const int64_t m0 = mbase + threadIdx.x, m = m0 < M ? m0 : M - 1;
-        s_fm[threadIdx.x] = a.w.xsc[2 * m + 1];       // 2^f_m
-        s_fm[kLRows + threadIdx.x] = a.w.xsc[2 * m];  // 2^-f_m
+        const int64_t m = mbase + threadIdx.x; // below the prepared row count
+        s_fm[threadIdx.x] = a.w.xsc[2 * m + 1];      // 2^f_m
+        s_fm[kLRows + threadIdx.x] = a.w.xsc[2 * m]; // 2^-f_m
     }
 
     // ---- stage fill --------------------------------------------------------
-    // Operand block slot = kLS wv + i (i < kLS), m-block slot % 8:
-    //   residual: K-step slot / 8 of the chunk (X rows)
-    //   core:     half (slot / 8) % 2 of t (slots 16..31 repeat 0..15)
-    //   correction: K-step slot / 16 of the pair, half (slot / 8) % 2 of s
-    // Code block j = kLVB wv + i holds the chunk of v-block j of the workgroup.
-    // Scale block st (residual stages): lane l covers v-block l / 2, rows
-    // 8 (l % 2) .. +7, for the group of K-step st (one block when a group
-    // spans the whole chunk).
-    const uint16_t *x16t = a.w.x16 + mbase * d;
-    const int64_t hsel = ((wv * kLS) >> 3) & 1; // (slot / 8) % 2 for this wave's slots
-    const uint16_t *t16t = a.w.t16 + (hsel * Mp + mbase) * kpad;
-    const uint16_t *s16t = a.w.s16 + (hsel * Mp + mbase) * rpad;
-    const u32x4 *lrp = (const u32x4 *)a.h.lr;
-    const u32x4 *r4p = (const u32x4 *)a.h.r4;
-    const int mb0 = (wv * kLS) & 7; // m-block of slot i is mb0 + i
-    uint32_t rowl[kLS];
-#pragma unroll
-    for (int i = 0; i < kLS; ++i) {
-        const int64_t r = 16 * (mb0 + i) + lr;
-        rowl[i] = (uint32_t)(r < rows_live ? r : rows_live - 1);
-    }
-    // scale rows this lane copies: v-block (lane / 2) of the workgroup
+    // Operand block b = kLS wv + i holds slot q = b / 8, m-block b % 8; so
+    // this wave copies slot fq, m-blocks fmb0 .. fmb0 + kLS - 1.
+    const int fq = (wv * kLS) >> 3, fmb0 = (wv * kLS) & 7;
+    const uint32_t *lrw = a.h.lr, *r4w = a.h.r4;
+    const int64_t chunk_words = nvb * 256; // uint32 words of one K-chunk of one stream
+    // residual-scale rows this lane copies: v-block lane / 2 of the workgroup
     const int64_t svb = wg_vb0 + (lane >> 1) < nvb ? wg_vb0 + (lane >> 1) : nvb - 1;
-    const uint32_t soff = (uint32_t)(svb * G * kVB + 8 * (lane & 1)); // + grp * 16
+    const int64_t soff = svb * G * kVB + 8 * (lane & 1); // + grp * 16
 
     auto stage_fill = [&](int64_t s, uint32_t *buf) {
-        const uint16_t *base;
-        uint32_t stride;
-        const u32x4 *cbase;
+        const int64_t hh = fq >> 1, half = fq & 1;
+        const uint16_t *base; // operand block of m-block 0 of the tile
+        int64_t mbstride;     // halfs between consecutive m-blocks
+        const uint32_t *cp[4];
+        int cw[4];
         int64_t kc = 0;
         if (s < p1) {
-            const int64_t ks0 = 2 * s + ((wv * kLS) >> 4), ks = ks0 < rst ? ks0 : rst - 1;
-            base = s16t + ks * kKStep;
-            stride = (uint32_t)rpad;
-            cbase = lrp + (a.na + (s < nc ? s : nc - 1)) * nvb * 64;
+            kc = s < nkc ? s : nkc - 1;
+            base = a.w.xsw + (mb16_0 * nks + kc * 4 + fq) * 512;
+            mbstride = nks * 512;
+            for (int q = 0; q < 4; ++q) {
+                cp[q] = r4w + kc * chunk_words;
+                cw[q] = q;
+            }
         } else if (s < p2) {
-            const int64_t ks = s - p1 < kst ? s - p1 : kst - 1;
-            base = t16t + ks * kKStep;
-            stride = (uint32_t)kpad;
-            cbase = lrp + (ks / 3) * nvb * 64;
+            const int64_t j = s - p1;
+            const int64_t ks0 = 2 * j + hh, ks = ks0 < rst ? ks0 : rst - 1;
+            base = a.w.ssw + ((mb16_0 * rst + ks) * 2 + half) * 512;
+            mbstride = rst * 2 * 512;
+            const uint32_t *c = lrw + (a.na + (j < a.nc ? j : a.nc - 1)) * chunk_words;
+            for (int q = 0; q < 4; ++q) {
+                cp[q] = c;
+                cw[q] = q;
+            }
         } else {
-            kc = s - p2 < nkc ? s - p2 : nkc - 1;
-            base = x16t + (kc * 4 + ((wv * kLS) >> 3)) * kKStep;
-            stride = (uint32_t)d;
-            cbase = r4p + kc * nvb * 64;
+            const int64_t j = s - p2;
+            const int64_t ks0 = 2 * j + hh, ks = ks0 < kst ? ks0 : kst - 1;
+            base = a.w.tsw + ((mb16_0 * kst + ks) * 2 + half) * 512;
+            mbstride = kst * 2 * 512;
+            const int64_t k0 = 2 * j < kst ? 2 * j : kst - 1, k1 = 2 * j + 1 < kst ? 2 * j + 1 : kst - 1;
+            cp[0] = cp[1] = lrw + (k0 / 3) * chunk_words;
+            cp[2] = cp[3] = lrw + (k1 / 3) * chunk_words;
+            cw[0] = (int)(k0 % 3);
+            cw[1] = 3;
+            cw[2] = (int)(k1 % 3);
+            cw[3] = 3;
         }
 #pragma unroll
         for (int i = 0; i < kLS; ++i)
-            lds_dma16(base + (rowl[i] * stride + 8 * lq), buf + (wv * kLS + i) * 256);
+            lds_dma16(base + (fmb0 + i) * mbstride + lane * 8, buf + (wv * kLS + i) * 256);
+        if (s < p2) { // one whole chunk per v-block: [lane][4 words], 16-byte copies
 #pragma unroll
-        for (int i = 0; i < kLVB; ++i) {
-            const int64_t vb = vb0 + i < nvb ? vb0 + i : nvb - 1;
-            lds_dma16(cbase + vb * 64 + lane, buf + kLCodeOff + (wv * kLVB + i) * 256);
+            for (int v = 0; v < kLVB; ++v)
+                lds_dma16(cp[0] + (vb[v] * 64 + lane) * 4, buf + kLCodeOff + (wv * kLVB + v) * 256);
+        } else { // words from up to two chunks: [4 words][lane], 4-byte copies
+#pragma unroll
+            for (int v = 0; v < kLVB; ++v)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    lds_dma4(cp[q] + (vb[v] * 64 + lane) * 4 + cw[q], buf + kLCodeOff + (wv * kLVB + v) * 256 + q * 64);
         }
-        if (s >= p2 && (GS == 4 ? wv == 0 : wv < 4)) { // kLW >= 4
+        if (s < p1 && (GS == 4 ? wv == 0 : wv < 4)) { // kLW >= 4
             const int64_t grp = GS == 4 ? kc : (kc * 4 + wv) / gsteps;
-            lds_dma16(a.h.srp + (soff + grp * kVB), buf + kLScOff + (GS == 4 ? 0 : wv) * 256);
+            lds_dma16(a.h.srp + (soff + grp * kVB), buf + kLScOff + (GS == 4 ? 0 : wv) * (kLVR * 8));
         }
     };
 
@@ -248,93 +352,73 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 #pragma unroll
         for (int v = 0; v < kLVB; ++v)
             T[mb][v] = zero;
-    const uint32_t magic16 = vgpr_const(kF16Magic);
-    auto afrag = [&](const uint32_t *buf, int blk) { return *(const u32x4 *)(buf + blk * 256 + lane * 4); };
-    auto codes = [&](const uint32_t *buf, u32x4(&c)[kLVB]) {
-#pragma unroll
-        for (int v = 0; v < kLVB; ++v)
-            c[v] = *(const u32x4 *)(buf + kLCodeOff + (wv * kLVB + v) * 256 + lane * 4);
-    };
+    const uint32_t magic = vgpr_const(kF16Magic);
+    // code words: residual and correction stages hold [lane][4 words] per
+    // v-block (read whole), core stages [4 words][lane]
+    auto chunk = [&](const uint32_t *buf, int v) { return *(const u32x4 *)(buf + kLCodeOff + (wv * kLVB + v) * 256 + lane * 4); };
+    auto code = [&](const uint32_t *buf, int v, int q) { return buf[kLCodeOff + (wv * kLVB + v) * 256 + q * 64 + lane]; };
 
-    // No branch surrounds an MFMA (the accumulator tile would be copied at
-    // every join): pad stages run with their codes masked to zero.
-    auto compute_c8 = [&](int64_t s, const uint32_t *buf) {
-        u32x4 c[kLVB];
-        codes(buf, c);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t live = (s < nc && 2 * s + hh < rst) ? 0xFFFFFFFFu : 0u;
-            u32x4 bq[kLVB];
-#pragma unroll
-            for (int v = 0; v < kLVB; ++v) {
-                u32x2 w2;
-                w2.x = hh == 0 ? c[v].x : c[v].z;
-                w2.y = hh == 0 ? c[v].y : c[v].w;
-                bq[v] = and4(c8_bf16(w2), ((nz >> (kLVB + v)) & 1u ? 0xFFFFFFFFu : 0u) & live);
-            }
-#pragma unroll
-            for (int mb = 0; mb < kLMB; ++mb) {
-                const u32x4 ah = afrag(buf, (2 * hh) * 8 + mb);
-                const u32x4 al = afrag(buf, (2 * hh + 1) * 8 + mb);
-#pragma unroll
-                for (int v = 0; v < kLVB; ++v) {
-                    T[mb][v] = mfma_bf16(ah, bq[v], T[mb][v]);
-                    T[mb][v] = mfma_bf16(al, bq[v], T[mb][v]);
-                }
-            }
-        }
-    };
-    auto compute_a5 = [&](int64_t s, const uint32_t *buf) {
-        u32x4 c[kLVB];
-        codes(buf, c);
-        const int64_t ks = s - p1;
-        const uint32_t live = ks < kst ? 0xFFFFFFFFu : 0u;
-        const int q = (int)(ks % 3);
-        u32x4 bq[kLVB];
-#pragma unroll
-        for (int v = 0; v < kLVB; ++v) {
-            const uint32_t wn = q == 0 ? c[v].x : q == 1 ? c[v].y : c[v].z;
-            const u32x4 b = a5_bf16_q(wn, c[v].w, q);
-            const uint32_t mk = ((nz >> v) & 1u ? 0xFFFFFFFFu : 0u) & live;
-            bq[v] = u32x4{unbias144(b.x) & mk, unbias144(b.y) & mk, unbias144(b.z) & mk, unbias144(b.w) & mk};
-        }
+    // the three stage kinds; no branch surrounds an MFMA (the accumulator
+    // tile would be copied at every join): slots past the end of a phase, and
+    // pad stages, have their B operands masked to zero
+    auto mfma_slot = [&](const uint32_t *buf, int q, const u32x4(&bq)[kLVB]) {
 #pragma unroll
         for (int mb = 0; mb < kLMB; ++mb) {
-            const u32x4 ah = afrag(buf, mb);
-            const u32x4 al = afrag(buf, 8 + mb);
+            const u32x4 ax = *(const u32x4 *)(buf + (q * 8 + mb) * 256 + lane * 4);
 #pragma unroll
-            for (int v = 0; v < kLVB; ++v) {
-                T[mb][v] = mfma_bf16(ah, bq[v], T[mb][v]);
-                T[mb][v] = mfma_bf16(al, bq[v], T[mb][v]);
-            }
+            for (int v = 0; v < kLVB; ++v)
+                T[mb][v] = mfma_f16(ax, bq[v], T[mb][v]);
         }
     };
     auto compute_r4 = [&](int64_t s, const uint32_t *buf) {
-        u32x4 c[kLVB];
-        codes(buf, c);
-        const uint32_t live = s - p2 < nkc ? 0xFFFFFFFFu : 0u;
+        const uint32_t live = s < nkc ? 0xFFFFFFFFu : 0u;
         const uint16_t *scb = (const uint16_t *)(buf + kLScOff);
-        uint32_t sc[kLVB][GS == 4 ? 1 : 4];
+        u32x4 c[kLVB];
 #pragma unroll
         for (int v = 0; v < kLVB; ++v)
+            c[v] = chunk(buf, v);
 #pragma unroll
-            for (int st = 0; st < (GS == 4 ? 1 : 4); ++st)
-                sc[v][st] = ((uint32_t)scb[(st * kLVR + wv * kLVB + v) * kVB + lr] * 0x10001u) & live;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int q = 0; q < 4; ++q) {
             u32x4 bq[kLVB];
 #pragma unroll
             for (int v = 0; v < kLVB; ++v) {
-                const uint32_t wd = st == 0 ? c[v].x : st == 1 ? c[v].y : st == 2 ? c[v].z : c[v].w;
-                bq[v] = r4_f16_scaled(wd, magic16, __builtin_bit_cast(f16x2, sc[v][GS == 4 ? 0 : st]));
+                const uint32_t sc = (uint32_t)scb[((GS == 4 ? 0 : q) * kLVR + wv * kLVB + v) * kVB + lr] * 0x10001u;
+                const uint32_t wd = q == 0 ? c[v].x : q == 1 ? c[v].y : q == 2 ? c[v].z : c[v].w;
+                bq[v] = and4(r4_f16(wd, magic, __builtin_bit_cast(f16x2, sc)), live);
             }
+            mfma_slot(buf, q, bq);
+        }
+    };
+    auto compute_c8 = [&](int64_t s, const uint32_t *buf) {
+        const int64_t j = s - p1;
 #pragma unroll
-            for (int mb = 0; mb < kLMB; ++mb) {
-                const u32x4 ax = afrag(buf, st * 8 + mb);
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t live = (j < a.nc && 2 * j + hh < rst) ? 0xFFFFFFFFu : 0u;
+            u32x4 bq[kLVB];
 #pragma unroll
-                for (int v = 0; v < kLVB; ++v)
-                    T[mb][v] = mfma_f16(ax, bq[v], T[mb][v]);
+            for (int v = 0; v < kLVB; ++v) {
+                const u32x4 c = chunk(buf, v);
+                bq[v] = and4(c8_f16(hh == 0 ? c.x : c.z, hh == 0 ? c.y : c.w, magic),
+                             ((nz >> (kLVB + v)) & 1u ? 0xFFFFFFFFu : 0u) & live);
             }
+            mfma_slot(buf, 2 * hh, bq);     // hi part of s
+            mfma_slot(buf, 2 * hh + 1, bq); // lo part of s
+        }
+    };
+    auto compute_a5 = [&](int64_t s, const uint32_t *buf) {
+        const int64_t j = s - p2;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int64_t ks = 2 * j + hh;
+            const uint32_t live = ks < kst ? 0xFFFFFFFFu : 0u;
+            const int qq = (int)(ks % 3);
+            u32x4 bq[kLVB];
+#pragma unroll
+            for (int v = 0; v < kLVB; ++v)
+                bq[v] = and4(a5_f16(code(buf, v, 2 * hh), code(buf, v, 2 * hh + 1), qq, magic),
+                             ((nz >> v) & 1u ? 0xFFFFFFFFu : 0u) & live);
+            mfma_slot(buf, 2 * hh, bq);
+            mfma_slot(buf, 2 * hh + 1, bq);
         }
     };
 
@@ -343,7 +427,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 
     // Stage s (even) computes from s_buf0 while stage s+1 fills s_buf1; the
     // barrier after it also waits for that fill.  No fill is left in flight
-    // past the last stage.
+    // past the last stage.  Every phase has an even stage count.
 #define ARCHEAD_LDS_PHASE(S0, S1, COMPUTE)                                          \
     for (int64_t s = (S0); s < (S1); s += 2) {                                     \
         stage_fill(s + 1, s_buf1);                                                 \
@@ -355,42 +439,32 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         __syncthreads();                                                           \
     }
 
-    // phase 1: correction (T = C8 . s)
-    ARCHEAD_LDS_PHASE(0, p1, compute_c8)
-    // T in units of sA (or of 1 where sA = 0)
+    // phase 1: residual, in units of 2^-(e_v + f_m)
+    ARCHEAD_LDS_PHASE(0, p1, compute_r4)
+    // to units of sC 2^-f_m
 #pragma unroll
     for (int v = 0; v < kLVB; ++v) {
-        const int64_t vb = vb0 + v < nvb ? vb0 + v : nvb - 1;
-        const float sa = h2f(a.h.sa[vb * kVB + lr]), sc = h2f(a.h.sc[vb * kVB + lr]);
-        const float ratio = sc / (sa != 0.f ? sa : 1.f);
+        const float f = a.h.rsc[vb[v] * kVB + lr] / pc(v);
 #pragma unroll
         for (int mb = 0; mb < kLMB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                T[mb][v][i] *= ratio;
+                T[mb][v][i] *= f;
     }
-    // phase 2: core (T += A5 . t)
-    ARCHEAD_LDS_PHASE(p1, p2, compute_a5)
-    // T in units of 2^-(e_v + f_m)
-    {
-        f32x4 fm[kLMB];
+    // phase 2: correction
+    ARCHEAD_LDS_PHASE(p1, p2, compute_c8)
+    // to units of sA 2^-f_m
+#pragma unroll
+    for (int v = 0; v < kLVB; ++v) {
+        const float f = pc(v) / pa(v);
 #pragma unroll
         for (int mb = 0; mb < kLMB; ++mb)
-            fm[mb] = *(const f32x4 *)(s_fm + mb * 16 + 4 * lq);
 #pragma unroll
-        for (int v = 0; v < kLVB; ++v) {
-            const int64_t vb = vb0 + v < nvb ? vb0 + v : nvb - 1;
-            const float sa = h2f(a.h.sa[vb * kVB + lr]);
-            const float conv = (sa != 0.f ? sa : 1.f) / a.h.rsc[vb * kVB + lr];
-#pragma unroll
-            for (int mb = 0; mb < kLMB; ++mb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    T[mb][v][i] *= conv * fm[mb][i];
-        }
+            for (int i = 0; i < 4; ++i)
+                T[mb][v][i] *= f;
     }
-    // phase 3: residual (T += X' . (sR' o R4))
-    ARCHEAD_LDS_PHASE(p2, nst, compute_r4)
+    // phase 3: core
+    ARCHEAD_LDS_PHASE(p2, nst, compute_a5)
 #undef ARCHEAD_LDS_PHASE
 
     // back to logits units; write logits and the workgroup's top-1 keys
@@ -403,9 +477,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
             uint64_t k = 0;
 #pragma unroll
             for (int v = 0; v < kLVB; ++v) {
-                const int64_t vb = vb0 + v < nvb ? vb0 + v : nvb - 1;
                 const int64_t row = (vb0 + v) * kVB + lr;
-                const float y = T[mb][v][i] * a.h.rsc[vb * kVB + lr] * fi[i];
+                const float y = T[mb][v][i] * pa(v) * fi[i];
                 if (m < M && vb0 + v < nvb && row < V) {
                     if (a.logits)
                         a.logits[m * V + row] = y;
@@ -439,17 +512,36 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+int64_t lds_max_n_part(const Shape &s) { return (s.nvb() + kLVR - 1) / kLVR; }
+
 int64_t lds_n_part(const DevHead &h, int64_t M)
 {
     (void)M;
     return lds_max_n_part(h.s);
 }
 
-int64_t lds_max_n_part(const Shape &s) { return (s.nvb() + kLVR - 1) / kLVR; }
-
-hipError_t launch_prep_x16(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
+hipError_t launch_prep_lds(const DevHead &h, const Work &w, const uint16_t *X, hipStream_t st)
 {
-    hipLaunchKernelGGL(prep_x16_kernel, dim3((unsigned)w.M), dim3(256), 0, st, X, h.s.d, w.x16, w.xsc);
+    PrepArgs a;
+    a.X = X;
+    a.tf32 = w.tf32;
+    a.sf32 = w.sf32;
+    a.M = w.M;
+    a.d = h.s.d;
+    a.k = h.s.k;
+    a.r = h.s.r;
+    a.kst = h.s.kst();
+    a.rst = h.s.rst();
+    a.kpad = h.s.kpad();
+    a.rpad = h.s.rpad();
+    a.xsw = w.xsw;
+    a.tsw = w.tsw;
+    a.ssw = w.ssw;
+    a.xsc = w.xsc;
+    const int64_t rows = (w.M + kLRows - 1) / kLRows * kLRows; // the tiles' rows, <= Mq
+    if (rows > w.Mq)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prep_lds_kernel, dim3((unsigned)rows), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -460,8 +552,8 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.h = h;
     a.w = w;
     a.w.n_part = lds_n_part(h, w.M);
-    if (w.M * a.w.n_part > w.part_cap)
-        return hipErrorInvalidValue; // argmax partials would not fit the workspace
+    if (w.M * a.w.n_part > w.part_cap || (w.M + kLRows - 1) / kLRows * kLRows > w.Mq)
+        return hipErrorInvalidValue; // the workspace does not hold this call
     a.logits = logits;
     a.want_argmax = argmax ? 1 : 0;
     a.gsteps = (int)(h.s.g / kKStep);
@@ -472,11 +564,9 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.nc = h.s.lr_nc();
     a.kst = h.s.kst();
     a.rst = h.s.rst();
-    a.kpad = h.s.kpad();
-    a.rpad = h.s.rpad();
-    a.p1 = (a.nc + 1) / 2 * 2;
-    a.p2 = a.p1 + (a.kst + 1) / 2 * 2;
-    a.nst = a.p2 + (a.nkc + 1) / 2 * 2;
+    a.nsr = (a.nkc + 1) / 2 * 2;                 // one K-chunk per stage
+    a.nsc = (a.nc + 1) / 2 * 2;                  // two correction K-steps per stage
+    a.nsa = ((a.kst + 1) / 2 + 1) / 2 * 2;      // two core K-steps per stage
     a.n_vr = a.w.n_part;
     a.n_mt = (w.M + kLRows - 1) / kLRows;
     a.n_tiles = a.n_vr * a.n_mt;
