@@ -35,7 +35,10 @@
  * Streams: every call that touches the device takes a hipStream_t (as void*;
  * NULL = the null stream).  Kernels are enqueued on that stream; the library
  * never synchronises it on the forward path and never allocates there once
- * the workspace is large enough (see archead_reserve).
+ * the workspace is large enough (see archead_reserve).  The forward calls of
+ * one handle share its workspace (including the work counters of the
+ * one-launch GEMV path): enqueue them on one stream, or order them with
+ * events; forward calls of one handle that overlap on the device race.
  *
  * Errors: every entry point returns an archead_status and never throws or
  * aborts.  Arguments are validated before anything is enqueued.  A HIP
@@ -65,10 +68,14 @@ typedef enum archead_status {
     ARCHEAD_EHIP = 5    /* a HIP runtime call failed                        */
 } archead_status;
 
-/* Kernel families for the vocabulary-tile step (archead_forward_path). */
+/* Kernel families for the vocabulary-tile step (archead_forward_path).
+ * GEMV runs the whole forward (projection, vocabulary tiles, argmax) as one
+ * kernel launch; it takes 1 <= M <= 4 and d a multiple of 512 (otherwise
+ * ARCHEAD_ESHAPE).  SKINNY and LDS take any M and launch the projection,
+ * the vocabulary tiles and the argmax reduction as separate kernels. */
 typedef enum archead_path {
     ARCHEAD_PATH_AUTO = 0,   /* chosen from M                                  */
-    ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV with wave shuffles, small M     */
+    ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV, one launch, M <= 4             */
     ARCHEAD_PATH_SKINNY = 2, /* register-dequantised MFMA, W streamed once     */
     ARCHEAD_PATH_LDS = 3     /* LDS-staged fp16-dequantised MFMA, large M      */
 } archead_path;

@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, sync, keys, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -106,6 +106,10 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(Mq) * 2 * 4);
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
+    L.sync = off;
+    off = align_up(off + 4 * 4);
+    L.keys = off;
+    off = align_up(off + size_t(kDecodeMaxM) * 8);
     L.total = off;
     return L;
 }
@@ -154,6 +158,8 @@ Work make_work(archead_t h, int64_t M)
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
     w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
+    w.sync = (uint32_t *)(b + L.sync);
+    w.keys = (uint64_t *)(b + L.keys);
     return w;
 }
 
@@ -353,11 +359,20 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     int chosen = path;
     if (chosen == ARCHEAD_PATH_AUTO)
         chosen = M >= kLdsMinM ? ARCHEAD_PATH_LDS : ARCHEAD_PATH_SKINNY;
-    if (chosen != ARCHEAD_PATH_SKINNY && chosen != ARCHEAD_PATH_LDS)
-        return fail(ARCHEAD_EINVAL, "path not available in this build");
+    if (chosen == ARCHEAD_PATH_GEMV && !gemv_decode_ok(h->dev, M))
+        return fail(ARCHEAD_ESHAPE, "the GEMV path takes M <= " + std::to_string(kDecodeMaxM) +
+                                        " and a head whose staging fits in LDS");
 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
+    if (chosen == ARCHEAD_PATH_GEMV) { // one launch: projection, tiles and argmax
+        if (ev0)
+            HIP_TRY(hipEventRecord(ev0, st));
+        HIP_TRY(launch_gemv_decode(h->dev, w, Xb, logits, argmax, st));
+        if (ev1)
+            HIP_TRY(hipEventRecord(ev1, st));
+        return ARCHEAD_OK;
+    }
     if (chosen == ARCHEAD_PATH_LDS) {
         HIP_TRY(launch_proj_mfma(h->dev, w, Xb, st));
         HIP_TRY(launch_prep_lds(h->dev, w, Xb, st));

@@ -143,6 +143,34 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
 }
 
+// bf16 halves of a packed pair as fp32 (exact)
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float i8(uint32_t w, int b) { return (float)(int8_t)(w >> (8 * b)); }
+
+// 16 int8 weights x 16 bf16 activations, fp32 accumulation
+__device__ __forceinline__ float dot16(u32x4 q, u32x4 x0, u32x4 x1)
+{
+    float s = 0.f;
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int e = 0; e < 4; ++e) {
+        s = __builtin_fmaf(bf_lo(xw[2 * e]), i8(qw[e], 0), s);
+        s = __builtin_fmaf(bf_hi(xw[2 * e]), i8(qw[e], 1), s);
+        s = __builtin_fmaf(bf_lo(xw[2 * e + 1]), i8(qw[e], 2), s);
+        s = __builtin_fmaf(bf_hi(xw[2 * e + 1]), i8(qw[e], 3), s);
+    }
+    return s;
+}
+
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // Order-preserving map of fp32 to uint32 (for max over packed keys); -0 is

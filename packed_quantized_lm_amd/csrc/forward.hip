@@ -38,33 +38,6 @@ struct ProjArgs {
     int ncolblk;
 };
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float i8(uint32_t w, int b) { return (float)(int8_t)(w >> (8 * b)); }
-
-// 16 int8 weights x 16 bf16 activations, fp32 accumulation
-__device__ __forceinline__ float dot16(u32x4 q, u32x4 x0, u32x4 x1)
-{
-    float s = 0.f;
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    for (int e = 0; e < 4; ++e) {
-        s = __builtin_fmaf(bf_lo(xw[2 * e]), i8(qw[e], 0), s);
-        s = __builtin_fmaf(bf_hi(xw[2 * e]), i8(qw[e], 1), s);
-        s = __builtin_fmaf(bf_lo(xw[2 * e + 1]), i8(qw[e], 2), s);
-        s = __builtin_fmaf(bf_hi(xw[2 * e + 1]), i8(qw[e], 3), s);
-    }
-    return s;
-}
-
 __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

@@ -120,7 +120,15 @@ struct Work {
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;
     int64_t part_cap;  // uint64 slots in part
+    // single-launch decode path: work counters {claimed projection columns,
+    // finished projection columns, finished workgroups, unused} and one
+    // argmax key per row, all zero between calls (the launch's last
+    // workgroup puts them back to zero)
+    uint32_t *sync;    // [4]
+    uint64_t *keys;    // [kDecodeMaxM]
 };
+
+constexpr int kDecodeMaxM = 4; // largest M of the single-launch decode path
 
 // Host relayout (pack.cpp).  Inputs in the canonical host layout; outputs are
 // host buffers in the device layout, sized by Shape::n_*.

@@ -1,0 +1,237 @@
+"""GPU parity of the single-launch GEMV decode path (projection, vocabulary
+tiles with VALU bf16-pair dot products, and argmax in one kernel) against the
+CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_argmax_ok, assert_logits_close, gpu_forward, say
+from oracle import forward as oracle_forward
+from packed_quantized_lm_amd.synth import make_config, random_small_head, to_bf16_bits, to_f16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from packed_quantized_lm_amd import load_library
+    load_library()
+    return torch.device("cuda:0")
+
+
+def load(fields):
+    from packed_quantized_lm_amd import PackedHead
+    return PackedHead(fields)
+
+
+SHAPES = [
+    # V,     d,    k,   r,   g,  M
+    (1, 512, 1, 1, 32, 1),
+    (15, 512, 8, 4, 64, 2),
+    (20, 512, 200, 60, 128, 1),     # 260 projection columns on 4 waves
+    (1000, 1024, 33, 7, 128, 3),
+    (3001, 512, 40, 20, 128, 4),
+    (4099, 1536, 64, 48, 256, 1),
+    (777, 512, 0, 16, 512, 2),      # no core term
+    (777, 1024, 40, 0, 128, 1),     # no correction term
+    (500, 512, 0, 0, 128, 1),       # residual only
+    (2500, 2560, 192, 48, 128, 4),  # the large-vocabulary head's d, k, r
+    (9000, 1536, 96, 33, 96, 2),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "V{}_d{}_k{}_r{}_g{}_M{}".format(*s))
+def test_gemv_shapes(shape):
+    V, d, k, r, g, M = shape
+    say(f"gemv {shape}")
+    f = random_small_head(V, d, k, r, g, M, seed=V * 5 + d + M, n_outliers=2, outlier_factor=20.0)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    y, a = gpu_forward(h, f["X"], path="gemv")
+    assert_logits_close(y, ref, what=str(shape))
+    assert_argmax_ok(a, y, ref, what=str(shape))
+    # argmax alone, logits alone, and a repeat: identical results
+    _, a2 = gpu_forward(h, f["X"], path="gemv", want_logits=False)
+    y3, _ = gpu_forward(h, f["X"], path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(a, a2)
+    assert np.array_equal(y, y3)
+
+
+def test_gemv_rejects_unsupported_shapes():
+    from packed_quantized_lm_amd.binding import ArcheadError
+    say("gemv rejections")
+    f = random_small_head(100, 256, 8, 4, 32, 5, seed=3)  # d = 256: 2 residual chunks
+    h = load(f)
+    with pytest.raises(ArcheadError):
+        gpu_forward(h, f["X"][:1], path="gemv")
+    h.close()
+    f = random_small_head(100, 512, 8, 4, 32, 5, seed=3)  # M = 5 > 4
+    h = load(f)
+    with pytest.raises(ArcheadError):
+        gpu_forward(h, f["X"], path="gemv")
+    y, _ = gpu_forward(h, f["X"][:4], path="gemv")
+    assert_logits_close(y, oracle_forward.forward(f, f["X"][:4]))
+    h.close()
+
+
+def test_gemv_one_hot_probes_are_bit_exact():
+    """One-hot hidden states read single integer codes back through every term."""
+    say("gemv one-hot probes")
+    rng = np.random.default_rng(4)
+    V, d, k, r, g = 300, 512, 40, 12, 128
+    G = d // g
+    one, zero = to_f16_bits(1.0), to_f16_bits(0.0)
+    base = {"V": V, "d": d, "k": k, "r": r, "g": g,
+            "A5": np.zeros((V, k), np.int8), "sA": np.full(V, zero, np.uint16),
+            "B8": np.zeros((k, d), np.int8), "sB": np.full(k, one, np.uint16),
+            "R4": np.zeros((V, d // 2), np.uint8), "sR": np.full((V, G), zero, np.uint16),
+            "C8": np.zeros((V, r), np.int8), "sC": np.full(V, zero, np.uint16),
+            "D8": np.zeros((r, d), np.int8), "sD": np.full((r, G), one, np.uint16)}
+
+    def onehot(cols):
+        x = np.zeros((len(cols), d))
+        x[np.arange(len(cols)), cols] = 1.0
+        return to_bf16_bits(x)
+
+    cols = [0, 129, 300, 511]
+    r4 = rng.integers(-8, 8, size=(V, d))
+    nib = (r4 & 0xF).astype(np.uint8)
+    h = load(dict(base, R4=(nib[:, 0::2] | (nib[:, 1::2] << 4)), sR=np.full((V, G), one, np.uint16)))
+    y, _ = gpu_forward(h, onehot(cols), path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(y, r4[:, cols].T.astype(np.float32))
+    a5 = rng.integers(-16, 16, size=(V, k)).astype(np.int8)
+    eye = np.zeros((k, d), np.int8)
+    eye[np.arange(k), np.arange(k)] = 1
+    h = load(dict(base, A5=a5, B8=eye, sA=np.full(V, one, np.uint16)))
+    kc = [0, 17, 33, 39]
+    y, _ = gpu_forward(h, onehot(kc), path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(y, a5[:, kc].T.astype(np.float32))
+    b8 = rng.integers(-128, 128, size=(k, d)).astype(np.int8)
+    a5d = np.zeros((V, k), np.int8)
+    a5d[np.arange(k), np.arange(k)] = 1
+    h = load(dict(base, A5=a5d, B8=b8, sA=np.full(V, one, np.uint16)))
+    y, _ = gpu_forward(h, onehot(cols), path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(y[:, :k], b8[:, cols].T.astype(np.float32))
+    assert np.all(y[:, k:] == 0)
+    c8 = rng.integers(-128, 128, size=(V, r)).astype(np.int8)
+    eye = np.zeros((r, d), np.int8)
+    eye[np.arange(r), np.arange(r)] = 1
+    h = load(dict(base, C8=c8, D8=eye, sC=np.full(V, one, np.uint16)))
+    rc = [0, 5, 11]
+    y, _ = gpu_forward(h, onehot(rc), path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(y, c8[:, rc].T.astype(np.float32))
+    d8 = rng.integers(-128, 128, size=(r, d)).astype(np.int8)
+    c8d = np.zeros((V, r), np.int8)
+    c8d[np.arange(r), np.arange(r)] = 1
+    h = load(dict(base, C8=c8d, D8=d8, sC=np.full(V, one, np.uint16)))
+    y, _ = gpu_forward(h, onehot(cols), path="gemv", want_argmax=False)
+    h.close()
+    assert np.array_equal(y[:, :r], d8[:, cols].T.astype(np.float32))
+
+
+def test_gemv_ties_resolve_to_the_lowest_index():
+    say("gemv argmax ties")
+    V, d = 700, 512
+    f = random_small_head(V, d, 8, 4, 128, 2, seed=6)
+    # rows 10, 333, 690 identical -> identical logits, in different workgroups
+    for name in ["A5", "R4", "C8", "sA", "sR", "sC"]:
+        f[name][333] = f[name][10]
+        f[name][690] = f[name][10]
+    # make row 10 (and its copies) the maximum for hidden state 0: residual
+    # codes +7 where X[0] > 0 and -8 elsewhere, with a large scale
+    x0_nonneg = (f["X"][0] & 0x8000) == 0  # bf16 sign bit
+    q = np.where(x0_nonneg, 7, -8)
+    nib = (q & 0xF).astype(np.uint8)
+    for v in (10, 333, 690):
+        f["R4"][v] = nib[0::2] | (nib[1::2] << 4)
+        f["sR"][v] = to_f16_bits(0.05)
+    h = load(f)
+    y, a = gpu_forward(h, f["X"], path="gemv")
+    h.close()
+    assert y[0, 10] == y[0, 333] == y[0, 690] == y[0].max()
+    assert a[0] == 10
+    assert np.array_equal(a, np.argmax(y, axis=1))
+
+
+def test_gemv_paths_interleave_on_one_handle():
+    """The single-launch path shares the workspace with the other paths; its
+    counters and keys must be back at zero after every call."""
+    say("gemv interleaved with other paths")
+    f = random_small_head(3000, 1024, 64, 16, 128, 4, seed=31)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    for path, M in [("gemv", 1), ("skinny", 4), ("gemv", 4), ("gemv", 2), ("lds", 3), ("gemv", 3)]:
+        y, a = gpu_forward(h, f["X"][:M], path=path)
+        assert_logits_close(y, ref[:M], what=f"{path} M={M}")
+        assert_argmax_ok(a, y, ref[:M], what=f"{path} M={M}")
+    h.close()
+
+
+def test_gemv_graph_replays_match_eager():
+    import torch
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    say("gemv graph replay")
+    f = random_small_head(5000, 1024, 96, 33, 128, 2, seed=78)
+    h = load(f)
+    X = x_tensor_from_bits(f["X"])
+    logits = torch.empty((2, 5000), dtype=torch.float32, device="cuda")
+    arg = torch.empty((2,), dtype=torch.int32, device="cuda")
+    h.forward_into(X, logits, arg, path="gemv")
+    torch.cuda.synchronize()
+    y0, a0 = logits.clone(), arg.clone()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        h.forward_into(X, logits, arg, path="gemv")
+        h.forward_into(X, logits, arg, path="gemv")
+    for rep in range(4):
+        logits.fill_(float("nan"))
+        arg.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, y0), f"replay {rep}: logits differ"
+        assert torch.equal(arg, a0), f"replay {rep}: argmax differs"
+        h.forward_into(X, logits, arg, path="gemv")  # eager work between replays
+        torch.cuda.synchronize()
+    del g
+    h.close()
+    ref = oracle_forward.forward(f, f["X"])
+    assert_logits_close(y0.cpu().numpy(), ref)
+
+
+def test_gemv_full_size_decode():
+    name = "qwen_m1"
+    say(f"gemv full size {name}: generating + loading")
+    c = make_config(name)
+    h = load(c)
+    say(f"gemv full size {name}: GPU forward")
+    y, a = gpu_forward(h, c["X"], path="gemv")
+    say(f"gemv full size {name}: oracle")
+    ref = oracle_forward.forward(c, c["X"])
+    ratio = assert_logits_close(y, ref, what=name)
+    assert_argmax_ok(a, y, ref, what=name)
+    h.close()
+    say(f"gemv full size {name}: worst |d|/(2e-3 rms) = {ratio:.3g}")
+
+
+def test_gemv_consecutive_calls_see_new_inputs():
+    """t and s are handed between workgroups through memory on every call;
+    calls with different hidden states must never see the previous call's."""
+    say("gemv consecutive calls with new inputs")
+    f = random_small_head(6000, 1024, 96, 33, 128, 4, seed=41)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    for rep in range(3):
+        for m in range(4):
+            y, a = gpu_forward(h, f["X"][m:m + 1], path="gemv")
+            assert_logits_close(y, ref[m:m + 1], what=f"rep {rep} row {m}")
+            assert_argmax_ok(a, y, ref[m:m + 1], what=f"rep {rep} row {m}")
+    h.close()
