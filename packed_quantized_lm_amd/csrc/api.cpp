@@ -107,9 +107,9 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
     L.sync = off;
-    off = align_up(off + 4 * 4);
+    off = align_up(off + kSyncWords * 4);
     L.keys = off;
-    off = align_up(off + size_t(kDecodeMaxM) * 8);
+    off = align_up(off + kKeyWords * 8);
     L.total = off;
     return L;
 }

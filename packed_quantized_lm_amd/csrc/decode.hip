@@ -19,16 +19,19 @@
 // share a row meet by two shuffles at the end.
 //
 // a1 runs inside the same launch: the first k + r waves of the grid each
-// take one column of t or s (claimed through a counter) and publish it with
-// a release increment of a second counter; a wave reads t and s only after
-// that counter reaches k + r, which it first helps along by claiming any
-// column still unclaimed, so no wave ever waits on a wave that has not
-// started.  The residual needs none of it, so the projection has long
-// finished when the first low-rank chunk arrives.
+// claim one column of t or s through a ticket counter, compute it, and
+// publish it through device-scope stores followed by an increment of a
+// second counter; a wave reads t and s only after that counter reaches
+// k + r, having first claimed and computed any column still unclaimed, so
+// no wave ever waits on a wave that has not started.  The residual needs
+// none of it, so the projection has long finished when the low-rank chunks
+// (placed in the middle of each wave's stream) arrive.
 //
-// a3 runs inside it too: each workgroup folds its top-1 keys into one 64-bit
-// atomic max per row, and the workgroup that finishes last turns the keys
-// into indices and zeroes the keys and the counters for the next call.
+// a3 runs inside it too: each workgroup folds its top-1 keys into 64-bit
+// atomic maxima, and the last workgroup to finish turns the keys into
+// indices and zeroes the keys and the counters for the next call.  Counters
+// and keys that many workgroups update are split over 16 addresses
+// (layout.hpp), since atomics on one address serialise.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -74,6 +77,20 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 
 constexpr int kDmaDevice = 16; // cache-policy operand of global_load_lds: sc1, device scope
 
+// Keeps one K-step's loads and arithmetic together: no memory access moves
+// across it in the optimiser (empty asm with a memory clobber) or in the
+// machine scheduler.
+__device__ __forceinline__ void step_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Marks an accumulator as read and written here (no instruction): the
+// arithmetic that feeds it cannot be sunk past this point, which would keep
+// the operands of several K-steps live at once.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
 constexpr uint32_t kBf16Neg136 = 0xC308C308u; // bf16 pair (-136, -136)
 constexpr uint32_t kBf16Neg144 = 0xC310C310u; // bf16 pair (-144, -144)
 
@@ -108,13 +125,17 @@ struct DPair {
 //   sr  [4*NV][G][16]        fp16  residual scales of its v-blocks
 //   x   [MF][d]              bf16  the hidden states
 //   ts  [4 waves] x { t hi [MF][kpad], t lo [MF][kpad], s hi [MF][rpad], s lo [MF][rpad] }  bf16
+//
+// A wave's chunk stream: the first residual K-chunks, then the low-rank
+// chunks, then the remaining residual K-chunks.  Placing the low-rank chunks
+// in the middle lets the projection finish long before they are needed and
+// keeps the waves from all reaching the low-rank work at once at the end.
 template <int MF, int GS>
 __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 {
     constexpr int NV = decode_nv(MF);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MF];
-    __shared__ int s_last;
     const uint16_t *s_sr = (const uint16_t *)smem;
     const uint16_t *s_x = (const uint16_t *)(smem + a.lds_x);
 
@@ -124,21 +145,27 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     const int64_t d = a.h.s.d, V = a.h.s.V, k = a.h.s.k;
     const int64_t kst = a.h.s.kst(), rst = a.h.s.rst(), kpad = a.h.s.kpad(), rpad = a.h.s.rpad();
     const int gsteps = GS ? GS : a.gsteps;
+    const int ntask = a.ntask;
     const int64_t wg_vb0 = (int64_t)blockIdx.x * 4 * NV;
     const int64_t vb0 = wg_vb0 + wv * NV;
     uint16_t *s_ts = (uint16_t *)(smem + a.lds_ts) + wv * (2 * MF * (kpad + rpad));
-    uint32_t *claimed = a.w.sync, *finished = a.w.sync + 1, *wg_done = a.w.sync + 2;
+    uint32_t *const sync = a.w.sync;
+    uint32_t *const finished = sync + sync_finished();
 
     int64_t vb[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
 
-    // ---- a1: one column of t or s per task, for every row m ----
-    auto claim = [&]() __attribute__((always_inline)) -> int {
+    // ---- a1: one column of t or s per task, for every row m.  Column
+    // i = g + kSyncGroups * t is ticket t of group g. ----
+    auto group_size = [&](int g) __attribute__((always_inline)) -> int {
+        return g < ntask ? (ntask - 1 - g) / kSyncGroups + 1 : 0;
+    };
+    auto claim = [&](int g) __attribute__((always_inline)) -> int {
         uint32_t t = 0;
         if (lane == 0)
-            t = __hip_atomic_fetch_add(claimed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            t = __hip_atomic_fetch_add(sync + sync_claimed(g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return (int)__builtin_amdgcn_readfirstlane(t);
     };
     auto run_task = [&](int i) __attribute__((always_inline)) {
@@ -153,12 +180,19 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         for (int64_t j00 = 0; j00 < d; j00 += 4096) {
             u32x4 wq[4];
             float sc[4];
+            // every load of the pass is issued before the first multiply
+            // (addresses clamped in range, results selected afterwards)
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int64_t j0 = j00 + 1024 * it + 16 * lane;
-                const bool ok = j0 < d;
-                wq[it] = ok ? *(const u32x4 *)(row + j0) : z;
-                sc[it] = (ok && isd) ? a.h.sd[c * G + j0 / a.h.s.g] : 1.0f;
+                const int64_t jc = j0 < d ? j0 : 0;
+                wq[it] = *(const u32x4 *)(row + jc);
+                sc[it] = isd ? a.h.sd[c * G + jc / a.h.s.g] : 1.0f;
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const bool ok = j00 + 1024 * it + 16 * lane < d;
+                wq[it] = ok ? wq[it] : z;
             }
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -207,36 +241,51 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                                                  kDmaDevice);
         }
     };
-    // t and s of the MF rows into this wave's LDS region, once every column
-    // is published.  Every column was claimed at the start by a running wave
-    // that computes it before it waits for anything, so the wait ends.
-    // The wait is bounded all the same (about 2^20 x 128 clocks, far beyond
-    // any projection), so that a launch always ends: if the counters were
-    // ever left inconsistent, the logits come out wrong instead.
-    auto wait_and_stage_ts = [&]() __attribute__((always_inline)) {
-        const uint32_t need = (uint32_t)a.ntask;
-        for (int spin = 0; spin < (1 << 20); ++spin) {
-            if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
-                break;
-            __builtin_amdgcn_s_sleep(2);
-        }
+    auto stage_ts = [&]() __attribute__((always_inline)) {
         const int64_t Mp = a.w.Mp;
         wave_dma16(a.w.t16, s_ts, MF * kpad / 8);
         wave_dma16(a.w.t16 + Mp * kpad, s_ts + MF * kpad, MF * kpad / 8);
         wave_dma16(a.w.s16, s_ts + 2 * MF * kpad, MF * rpad / 8);
         wave_dma16(a.w.s16 + Mp * rpad, s_ts + 2 * MF * kpad + MF * rpad, MF * rpad / 8);
-        // the copies must land before the first LDS read of t and s; the
-        // compiler's own tracking of direct-to-LDS copies does not cover
-        // every read of the region, so wait here explicitly
-        wait_vm_all();
+    };
+    // t and s of the MF rows into this wave's LDS region once every column
+    // is published.  A wave that finds columns missing first claims and
+    // computes every column still unclaimed, so it waits only for columns
+    // held by running waves, which compute them without waiting; the wait
+    // is bounded all the same (about 2^20 x 128 clocks), so that a launch
+    // always ends even if the counters were left inconsistent (the logits
+    // would then be wrong).
+    auto wait_and_stage_ts = [&]() __attribute__((always_inline)) {
+        const uint32_t need = (uint32_t)ntask;
+        if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+            for (int g = 0; g < kSyncGroups; ++g)
+                for (;;) {
+                    const int t = claim(g);
+                    if (t >= group_size(g))
+                        break;
+                    run_task(g + kSyncGroups * t);
+                }
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
+                    break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        stage_ts();
     };
 
-    // ---- chunk stream: residual chunks 0 .. nkc-1, then the low-rank chunks ----
-    const int64_t ntot = nkc + nlr, npairs = (ntot + 1) / 2;
+    // ---- the chunk stream, in pairs of chunks ----
+    const int64_t nrp = nkc / 2, nlp = nlr / 2;                  // both even
+    // residual pairs before the low-rank ones (even; with no low-rank
+    // chunks, all but the last two)
+    const int64_t nrp1 = nlr > 0 ? ((nrp / 2) & ~int64_t(1)) : nrp - 2;
+    const int64_t c1 = 2 * nrp1, c2 = c1 + nlr, npairs = nrp + nlp;
     const u32x4 *lrp = (const u32x4 *)a.h.lr;
     const u32x4 *r4p = (const u32x4 *)a.h.r4;
     auto load_chunk = [&](DChunk<NV> &c, int64_t ci) __attribute__((always_inline)) {
-        const u32x4 *base = ci < nkc ? r4p + ci * nvb * 64 : lrp + (ci - nkc) * nvb * 64;
+        const u32x4 *base = ci < c1   ? r4p + ci * nvb * 64
+                            : ci < c2 ? lrp + (ci - c1) * nvb * 64
+                                      : r4p + (ci - nlr) * nvb * 64;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             c.q[v] = __builtin_nontemporal_load(&base[vb[v] * 64 + lane]);
@@ -246,13 +295,13 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         load_chunk(p.h1, 2 * pi + 1);
     };
 
-    // projection columns: wave gw takes one claim for each of the indices
-    // gw, gw + nw, gw + 2 nw, ... below k + r (nw waves in the grid), so the
-    // grid makes exactly k + r claims, all at its start, and every column is
-    // claimed by a wave that is running
+    // projection columns: wave gw owns the indices i = gw, gw + nw, ... below
+    // k + r (nw waves in the grid) and takes one ticket of group i % 16 for
+    // each, so the grid's tickets at its start cover every column exactly
+    // once.  The first ticket is requested before anything else.
     const int64_t gw = (int64_t)blockIdx.x * 4 + wv, nw = (int64_t)a.nwg * 4;
-    const int ntask_here = gw < a.ntask ? (int)((a.ntask - 1 - gw) / nw + 1) : 0;
-    int task = ntask_here > 0 ? claim() : a.ntask;
+    const int g0 = (int)(gw % kSyncGroups);
+    const int t0 = gw < ntask ? claim(g0) : 0;
 
     DPair<NV> P0, P1;
     load_pair(P0, 0);
@@ -274,26 +323,30 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         }
     }
     __syncthreads();
-    for (int j = 0; j < ntask_here; ++j) {
-        if (j > 0)
-            task = claim();
-        if (task < a.ntask) // always true while the counters start at zero
-            run_task(task);
+    if (gw < ntask) {
+        if (t0 < group_size(g0))
+            run_task(g0 + kSyncGroups * t0);
+        for (int64_t i = gw + nw; i < ntask; i += nw) {
+            const int g = (int)(i % kSyncGroups);
+            const int t = claim(g);
+            if (t < group_size(g))
+                run_task(g + kSyncGroups * t);
+        }
     }
 
     // per-lane partial sums over the lane's columns
-    float tot[NV][MF], g[NV][MF], xn[MF], ga[NV][MF], gc[NV][MF], nt[MF];
+    float tot[NV][MF], g[NV][MF], xn[MF];
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
-        xn[m] = nt[m] = 0.f;
+        xn[m] = 0.f;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-            tot[v][m] = g[v][m] = ga[v][m] = gc[v][m] = 0.f;
+            tot[v][m] = g[v][m] = 0.f;
     }
     const uint32_t kMagic = vgpr_const(kBf16Magic);
     const uint32_t c136 = vgpr_const(kBf16Neg136), c144 = vgpr_const(kBf16Neg144);
 
-    // residual chunk kc: 4 K-steps; each g-group is folded with its scale
+    // residual K-chunk kc: 4 K-steps; each g-group is folded with its scale
     // when it ends: tot += sR (sum x (q + 136) - 136 sum x)
     auto res_chunk = [&](const DChunk<NV> &c, int64_t kc) __attribute__((always_inline)) {
 #pragma unroll
@@ -329,13 +382,22 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 for (int m = 0; m < MF; ++m)
                     xn[m] = 0.f;
             }
-            // one K-step at a time: the dequantised codes of later K-steps
-            // are not hoisted into registers early
-            __builtin_amdgcn_sched_barrier(0);
+            // one K-step at a time: the hidden-state fragments and
+            // dequantised codes of later K-steps are not hoisted into
+            // registers early, nor this step's arithmetic sunk late
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                pin(xn[m]);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    pin(g[v][m]);
+            }
+            step_fence();
         }
     };
     // low-rank chunk j: three core K-steps (A5 + 16 against t) or two
     // correction K-steps (C8 against s); K-steps beyond the rank are skipped
+    float ga[NV][MF], gc[NV][MF], nt[MF];
     const uint16_t *s_t = s_ts, *s_s = s_ts + 2 * MF * kpad;
     auto lr_chunk = [&](const DChunk<NV> &c, int64_t j) __attribute__((always_inline)) {
         if (j < na) {
@@ -359,7 +421,14 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     for (int m = 0; m < MF; ++m)
                         ga[v][m] = dot8(tl[m], b, dot8(th[m], b, ga[v][m]));
                 }
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    pin(nt[m]);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        pin(ga[v][m]);
+                }
+                step_fence();
             }
         } else {
 #pragma unroll
@@ -383,63 +452,100 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     for (int m = 0; m < MF; ++m)
                         gc[v][m] = dot8(sl[m], b, dot8(sh[m], b, gc[v][m]));
                 }
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        pin(gc[v][m]);
+                step_fence();
             }
         }
     };
-    // residual pairs (nkc / 2 of them, an even count), then the low-rank
-    // pairs (nlr / 2, also even); the loads of the last residual pairs
-    // already fetch the first low-rank chunks.  The last iteration issues no
-    // loads (no load sits under a branch, which would make the compiler copy
-    // the prefetch buffers).
-    const int64_t nrp = nkc / 2;
-    auto res_iter = [&](int64_t pi, bool load) __attribute__((always_inline)) {
-        res_chunk(P0.h0, 2 * pi);
-        res_chunk(P0.h1, 2 * pi + 1);
-        if (load)
-            load_pair(P0, pi + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        res_chunk(P1.h0, 2 * pi + 2);
-        res_chunk(P1.h1, 2 * pi + 3);
-        if (load)
-            load_pair(P1, pi + 3);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto lr_iter = [&](int64_t pi, bool load) __attribute__((always_inline)) {
-        lr_chunk(P0.h0, 2 * pi - nkc);
-        lr_chunk(P0.h1, 2 * pi + 1 - nkc);
-        if (load)
-            load_pair(P0, pi + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        lr_chunk(P1.h0, 2 * pi + 2 - nkc);
-        lr_chunk(P1.h1, 2 * pi + 3 - nkc);
-        if (load)
-            load_pair(P1, pi + 3);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    int64_t pi = 0;
-    for (; pi + 2 < npairs; pi += 2) {
-        if (pi >= nrp)
-            break;
-        res_iter(pi, true);
-    }
-    if (nlr == 0) {
-        res_iter(pi, false);
-    } else {
-        wait_and_stage_ts();
-        for (; pi + 2 < npairs; pi += 2)
-            lr_iter(pi, true);
-        lr_iter(pi, false);
-    }
 
-    // ---- logits: the four lanes of a row add their partial sums ----
+    // two pairs per iteration: residual pairs pi, pi + 1 (K-chunks kc0 ..
+    // kc0 + 3) or low-rank pairs pi, pi + 1; the last iteration issues no
+    // loads (no load sits under a branch, which would make the compiler copy
+    // the prefetch buffers)
+    auto res_iter = [&](int64_t pi, int64_t kc0, bool load) __attribute__((always_inline)) {
+        res_chunk(P0.h0, kc0);
+        res_chunk(P0.h1, kc0 + 1);
+        if (load)
+            load_pair(P0, pi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        res_chunk(P1.h0, kc0 + 2);
+        res_chunk(P1.h1, kc0 + 3);
+        if (load)
+            load_pair(P1, pi + 3);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto lr_iter = [&](int64_t pi) __attribute__((always_inline)) {
+        lr_chunk(P0.h0, 2 * pi - c1);
+        lr_chunk(P0.h1, 2 * pi + 1 - c1);
+        load_pair(P0, pi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        lr_chunk(P1.h0, 2 * pi + 2 - c1);
+        lr_chunk(P1.h1, 2 * pi + 3 - c1);
+        load_pair(P1, pi + 3);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One control path for every shape (separate paths for the cases made
+    // the register allocator spill the prefetch buffers).  The last
+    // iteration before the low-rank pairs reads the published-column count,
+    // issued ahead of the iteration's prefetch so that waiting for it costs
+    // nothing (loads complete in order).  If it shows every column, t and s
+    // are copied to LDS with no further wait (a copy issued inside the loops
+    // would cost registers).
+    int64_t pi = 0;
+    for (; pi + 2 < nrp1; pi += 2)
+        res_iter(pi, 2 * pi, true);
+    bool ready = false;
+    if (nrp1 >= 2) {
+        const uint32_t seen = __hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        res_iter(pi, 2 * pi, true);
+        pi += 2;
+        ready = __builtin_amdgcn_readfirstlane(seen) >= (uint32_t)ntask;
+    }
+    if (nlr > 0) {
+        if (ready)
+            stage_ts();
+        else
+            wait_and_stage_ts();
+    }
+    // row scales of the low-rank terms, consumed after the low-rank pairs
     float sa[NV], sc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         sa[v] = h2f(a.h.sa[vb[v] * kVB + lr]);
         sc[v] = h2f(a.h.sc[vb[v] * kVB + lr]);
     }
+    // the copies of t and s must have landed before the first LDS read of
+    // them (the compiler's own tracking of direct-to-LDS copies does not
+    // cover every read of the region)
+    wait_vm_all();
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+        nt[m] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            ga[v][m] = gc[v][m] = 0.f;
+    }
+    // at least two residual pairs follow, so every iteration prefetches
+    for (; pi < nrp1 + nlp; pi += 2)
+        lr_iter(pi);
+    // tot += sA (A5 t - 144 sum t) + sC (C8 s), per lane
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+            tot[v][m] = __builtin_fmaf(sa[v], ga[v][m] + nt[m], __builtin_fmaf(sc[v], gc[v][m], tot[v][m]));
+    for (; pi + 2 < npairs; pi += 2)
+        res_iter(pi, 2 * pi - nlr, true);
+    res_iter(pi, 2 * pi - nlr, false);
+
+    // ---- logits: the four lanes of a row add their partial sums ----
     uint64_t key[MF];
+    float yv[NV][MF];
 #pragma unroll
     for (int m = 0; m < MF; ++m)
         key[m] = 0;
@@ -448,18 +554,31 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
-            float y = __builtin_fmaf(sa[v], ga[v][m] + nt[m], __builtin_fmaf(sc[v], gc[v][m], tot[v][m]));
+            float y = tot[v][m];
             y += __shfl_xor(y, 16);
             y += __shfl_xor(y, 32);
-            if (row < V) {
-                if (a.logits && lq == 0)
-                    a.logits[m * V + row] = y;
+            yv[v][m] = y;
+            if (row < V)
                 key[m] = umax64(key[m], argmax_key(y, (uint32_t)row));
-            }
         }
     }
+    auto store_logits = [&]() __attribute__((always_inline)) {
+        if (!a.logits)
+            return;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                if (row < V && lq == 0)
+                    a.logits[m * V + row] = yv[v][m];
+        }
+    };
 
-    // ---- a3: workgroup maximum per row, then one atomic max per row ----
+    // ---- a3: workgroup maximum per row; then per slot of workgroups (the
+    // workgroups b with b % nslot == s) an atomic max and a count, and the
+    // last workgroup of each slot passes its slot's keys on to the grid's;
+    // the last slot resolves the keys and resets every counter ----
     if (a.argmax) {
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
@@ -471,34 +590,56 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             if (lane == 0)
                 red[wv][m] = kk;
         }
-        __syncthreads();
-        if (threadIdx.x < MF) {
-            const int m = threadIdx.x;
-            const uint64_t kk = umax64(umax64(red[0][m], red[1][m]), umax64(red[2][m], red[3][m]));
-            __hip_atomic_fetch_max(a.w.keys + m, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every wave of the workgroup is past its last use of the counters (and
+    // has its keys in LDS); no stores are outstanding yet, so the barrier's
+    // wait for memory is short
+    __syncthreads();
+    if (wv != 0) {
+        store_logits();
+        return;
+    }
+    // wave 0.  Device-scope atomics are performed at the device's coherence
+    // point; each is complete before the count that follows it.
+    const int nslot = a.nwg < kSyncGroups ? a.nwg : kSyncGroups;
+    const int slot = (int)(blockIdx.x % nslot);
+    const uint32_t slot_size = (uint32_t)((a.nwg - 1 - slot) / nslot + 1);
+    uint64_t *const slot_key = a.w.keys + slot * 32, *const top_key = a.w.keys + kSyncGroups * 32;
+    if (a.argmax && lane < MF) {
+        const uint64_t kk = umax64(umax64(red[0][lane], red[1][lane]), umax64(red[2][lane], red[3][lane]));
+        __hip_atomic_fetch_max(slot_key + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vm_all();
+    uint32_t prev = 0;
+    if (lane == 0)
+        prev = __hip_atomic_fetch_add(sync + sync_slot_done(slot), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
+        if (lane == 0)
+            __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (a.argmax && lane < MF) {
+            const uint64_t kk =
+                __hip_atomic_exchange(slot_key + lane, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(top_key + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vm_all();
+        uint32_t prev2 = 0;
+        if (lane == 0)
+            prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
+            if (a.argmax && lane < MF) {
+                const uint64_t kk =
+                    __hip_atomic_exchange(top_key + lane, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+            }
+            if (lane < kSyncGroups)
+                __hip_atomic_store(sync + sync_claimed(lane), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) {
+                __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
-    // the last workgroup to finish resolves the keys and resets the counters;
-    // the barrier waits for the key updates (device-scope atomics) to complete
-    // before the workgroup counts itself done
-    __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(wg_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 (uint32_t)(a.nwg - 1);
-    __syncthreads();
-    if (s_last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (a.argmax && threadIdx.x < MF) {
-            const uint64_t kk = __hip_atomic_exchange(a.w.keys + threadIdx.x, (uint64_t)0, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-            a.argmax[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-        }
-        if (threadIdx.x == 0) {
-            __hip_atomic_store(claimed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(wg_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    store_logits();
 }
 
 // ---------------------------------------------------------------------------

@@ -120,15 +120,31 @@ struct Work {
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;
     int64_t part_cap;  // uint64 slots in part
-    // single-launch decode path: work counters {claimed projection columns,
-    // finished projection columns, finished workgroups, unused} and one
-    // argmax key per row, all zero between calls (the launch's last
-    // workgroup puts them back to zero)
-    uint32_t *sync;    // [4]
-    uint64_t *keys;    // [kDecodeMaxM]
+    // single-launch decode path: work counters and argmax keys (layout
+    // below), all zero between calls (the launch puts them back to zero)
+    uint32_t *sync;    // [kSyncWords]
+    uint64_t *keys;    // [kKeyWords]
 };
 
 constexpr int kDecodeMaxM = 4; // largest M of the single-launch decode path
+
+// Work counters of the single-launch decode path.  Atomics on one address
+// serialise (about 10 ns each), so counters that many workgroups update are
+// split into kSyncGroups copies, each in its own 256-byte line:
+//   claimed[g]    projection columns of group g claimed so far
+//   slot_done[s]  workgroups of slot s finished
+//   finished      projection columns published
+//   top_done      slots finished
+// and the argmax keys: per slot s, keys[s * 32 + m]; the grid's,
+// keys[kSyncGroups * 32 + m], m < kDecodeMaxM.
+constexpr int kSyncGroups = 16;
+constexpr int kSyncStride = 64; // uint32 per 256-byte line
+constexpr size_t kSyncWords = size_t(2 * kSyncGroups + 2) * kSyncStride;
+constexpr size_t kKeyWords = size_t(kSyncGroups + 1) * 32;
+__host__ __device__ constexpr size_t sync_claimed(int g) { return size_t(g) * kSyncStride; }
+__host__ __device__ constexpr size_t sync_slot_done(int s) { return size_t(kSyncGroups + s) * kSyncStride; }
+__host__ __device__ constexpr size_t sync_finished() { return size_t(2 * kSyncGroups) * kSyncStride; }
+__host__ __device__ constexpr size_t sync_top_done() { return size_t(2 * kSyncGroups + 1) * kSyncStride; }
 
 // Host relayout (pack.cpp).  Inputs in the canonical host layout; outputs are
 // host buffers in the device layout, sized by Shape::n_*.
