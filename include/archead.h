@@ -70,12 +70,14 @@ typedef enum archead_status {
 
 /* Kernel families for the vocabulary-tile step (archead_forward_path).
  * GEMV runs the whole forward (projection, vocabulary tiles, argmax) as one
- * kernel launch; it takes 1 <= M <= 4 and d a multiple of 512 (otherwise
- * ARCHEAD_ESHAPE).  SKINNY and LDS take any M and launch the projection,
- * the vocabulary tiles and the argmax reduction as separate kernels. */
+ * kernel launch; it takes d a multiple of 512 and M = 1, or M = 2 with
+ * g = 128 (otherwise ARCHEAD_ESHAPE).  SKINNY runs as one launch too at M = 1 when d is a
+ * multiple of 512 and g = 128, and otherwise, like LDS, launches the
+ * projection, the vocabulary tiles and the argmax reduction as separate
+ * kernels; both take any M. */
 typedef enum archead_path {
     ARCHEAD_PATH_AUTO = 0,   /* chosen from M                                  */
-    ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV, one launch, M <= 4             */
+    ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV, one launch, M <= 2             */
     ARCHEAD_PATH_SKINNY = 2, /* register-dequantised MFMA, W streamed once     */
     ARCHEAD_PATH_LDS = 3     /* LDS-staged fp16-dequantised MFMA, large M      */
 } archead_path;

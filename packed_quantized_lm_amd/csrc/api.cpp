@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, sync, keys, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, sync, keys, colflag, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -110,6 +110,8 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + kSyncWords * 4);
     L.keys = off;
     off = align_up(off + kKeyWords * 8);
+    L.colflag = off;
+    off = align_up(off + size_t(std::max<int64_t>(s.k + s.r, 1)) * 4);
     L.total = off;
     return L;
 }
@@ -160,6 +162,7 @@ Work make_work(archead_t h, int64_t M)
     w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
     w.sync = (uint32_t *)(b + L.sync);
     w.keys = (uint64_t *)(b + L.keys);
+    w.colflag = (uint32_t *)(b + L.colflag);
     return w;
 }
 
@@ -359,16 +362,19 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     int chosen = path;
     if (chosen == ARCHEAD_PATH_AUTO)
         chosen = M >= kLdsMinM ? ARCHEAD_PATH_LDS : ARCHEAD_PATH_SKINNY;
-    if (chosen == ARCHEAD_PATH_GEMV && !gemv_decode_ok(h->dev, M))
+    if (chosen == ARCHEAD_PATH_GEMV && !decode_ok(h->dev, M, false))
         return fail(ARCHEAD_ESHAPE, "the GEMV path takes M <= " + std::to_string(kDecodeMaxM) +
-                                        " and a head whose staging fits in LDS");
+                                        ", d a multiple of 512 and a head whose staging fits in LDS");
+    // the skinny path runs as one launch where the shape allows
+    const bool one_launch = chosen == ARCHEAD_PATH_GEMV ||
+                            (chosen == ARCHEAD_PATH_SKINNY && decode_ok(h->dev, M, true));
 
     Work w = make_work(h, M);
     const uint16_t *Xb = (const uint16_t *)X;
-    if (chosen == ARCHEAD_PATH_GEMV) { // one launch: projection, tiles and argmax
+    if (one_launch) { // projection, tiles and argmax
         if (ev0)
             HIP_TRY(hipEventRecord(ev0, st));
-        HIP_TRY(launch_gemv_decode(h->dev, w, Xb, logits, argmax, st));
+        HIP_TRY(launch_decode(h->dev, w, Xb, logits, argmax, chosen == ARCHEAD_PATH_SKINNY, st));
         if (ev1)
             HIP_TRY(hipEventRecord(ev1, st));
         return ARCHEAD_OK;

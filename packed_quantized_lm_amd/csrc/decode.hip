@@ -1,5 +1,6 @@
-// decode.hip -- the whole packed ARCHead forward for M <= 4 in one launch,
-// with VALU dot products (bf16 pairs into fp32).
+// decode.hip -- the whole packed ARCHead forward for M <= 2 in one launch,
+// with VALU dot products (bf16 pairs into fp32) or, at M = 1, matrix-core
+// products.
 //
 // ARCHead paper, section 3.2, eq 7 with W_d from eq 3 and the INT8 factors
 // of the text after eq 7:
@@ -18,14 +19,12 @@
 // or of the bf16 hi/lo parts of t and s (low-rank).  The four lanes that
 // share a row meet by two shuffles at the end.
 //
-// a1 runs inside the same launch: the first k + r waves of the grid each
-// claim one column of t or s through a ticket counter, compute it, and
-// publish it through device-scope stores followed by an increment of a
-// second counter; a wave reads t and s only after that counter reaches
-// k + r, having first claimed and computed any column still unclaimed, so
-// no wave ever waits on a wave that has not started.  The residual needs
-// none of it, so the projection has long finished when the low-rank chunks
-// (placed in the middle of each wave's stream) arrive.
+// a1 runs inside the same launch: wave w of the grid computes columns w,
+// w + nw, ... of t and s (nw waves) and publishes them through device-scope
+// stores followed by an increment of a counter.  The residual needs none of
+// it; three quarters through its residual a wave reads the count once, and if
+// every column is published it copies t and s to LDS, and otherwise computes
+// them itself.  No wave ever waits for another wave.
 //
 // a3 runs inside it too: each workgroup folds its top-1 keys into 64-bit
 // atomic maxima, and the last workgroup to finish turns the keys into
@@ -36,6 +35,8 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+
+#include <algorithm>
 
 namespace archead {
 
@@ -90,6 +91,7 @@ __device__ __forceinline__ void step_fence()
 // arithmetic that feeds it cannot be sunk past this point, which would keep
 // the operands of several K-steps live at once.
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin4(f32x4 &x) { asm volatile("" : "+v"(x)); }
 
 constexpr uint32_t kBf16Neg136 = 0xC308C308u; // bf16 pair (-136, -136)
 constexpr uint32_t kBf16Neg144 = 0xC310C310u; // bf16 pair (-144, -144)
@@ -103,13 +105,15 @@ struct DecodeArgs {
     int64_t nvb, nkc, G, na, nlr;
     int gsteps;
     int ntask;       // k + r projection columns
-    int nwg;         // workgroups in the grid
+    int ntwg;        // projection-only workgroups, first in the grid (0: the
+                     // streaming waves compute the columns themselves)
+    int nwg;         // streaming workgroups, after them
     unsigned lds_x, lds_ts; // byte offsets of the X and t/s regions (sr at 0)
 };
 
-// v-blocks per wave: five while the accumulators of MF rows leave room for
-// two prefetch pairs at two waves per SIMD, fewer above
-constexpr int decode_nv(int MF) { return MF <= 2 ? 5 : 3; }
+// v-blocks per wave: five at M = 1, four at M = 2 (whose accumulators need
+// the registers), with two prefetch pairs at two waves per SIMD
+constexpr int decode_nv(int MF) { return MF == 1 ? 5 : 4; }
 
 template <int NV>
 struct DChunk {
@@ -126,13 +130,14 @@ struct DPair {
 //   x   [MF][d]              bf16  the hidden states
 //   ts  [4 waves] x { t hi [MF][kpad], t lo [MF][kpad], s hi [MF][rpad], s lo [MF][rpad] }  bf16
 //
-// A wave's chunk stream: the first residual K-chunks, then the low-rank
-// chunks, then the remaining residual K-chunks.  Placing the low-rank chunks
+// A wave's chunk stream: the first three quarters of the residual K-chunks,
+// then the low-rank chunks, then the remaining residual K-chunks.  Placing the low-rank chunks
 // in the middle lets the projection finish long before they are needed and
 // keeps the waves from all reaching the low-rank work at once at the end.
-template <int MF, int GS>
+template <int MF, int GS, bool MX>
 __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 {
+    static_assert(!MX || GS == 4, "the matrix-core variant folds one g = 128 group per chunk");
     constexpr int NV = decode_nv(MF);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MF];
@@ -146,29 +151,23 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     const int64_t kst = a.h.s.kst(), rst = a.h.s.rst(), kpad = a.h.s.kpad(), rpad = a.h.s.rpad();
     const int gsteps = GS ? GS : a.gsteps;
     const int ntask = a.ntask;
-    const int64_t wg_vb0 = (int64_t)blockIdx.x * 4 * NV;
+    const bool proj_wg = (int)blockIdx.x < a.ntwg;
+    const int64_t bid = (int64_t)blockIdx.x - a.ntwg; // streaming workgroup index
+    const int64_t wg_vb0 = (proj_wg ? 0 : bid) * 4 * NV;
     const int64_t vb0 = wg_vb0 + wv * NV;
     uint16_t *s_ts = (uint16_t *)(smem + a.lds_ts) + wv * (2 * MF * (kpad + rpad));
     uint32_t *const sync = a.w.sync;
-    uint32_t *const finished = sync + sync_finished();
+    // the call's tag: column flags equal to it were written by this call
+    const uint32_t epoch = __hip_atomic_load(sync + sync_epoch(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     int64_t vb[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
 
-    // ---- a1: one column of t or s per task, for every row m.  Column
-    // i = g + kSyncGroups * t is ticket t of group g. ----
-    auto group_size = [&](int g) __attribute__((always_inline)) -> int {
-        return g < ntask ? (ntask - 1 - g) / kSyncGroups + 1 : 0;
-    };
-    auto claim = [&](int g) __attribute__((always_inline)) -> int {
-        uint32_t t = 0;
-        if (lane == 0)
-            t = __hip_atomic_fetch_add(sync + sync_claimed(g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return (int)__builtin_amdgcn_readfirstlane(t);
-    };
-    auto run_task = [&](int i) __attribute__((always_inline)) {
+    // ---- a1: column i of t (i < k) or s (i >= k) for every row m, as a
+    // bf16 hi/lo pair in lane m ----
+    auto column = [&](int i, uint16_t (&hi)[MF], uint16_t (&lo)[MF]) __attribute__((always_inline)) {
         const bool isd = i >= k;
         const int64_t c = isd ? i - k : i;
         const int8_t *row = isd ? a.h.d8 + c * d : a.h.b8 + c * d;
@@ -207,27 +206,35 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             }
         }
 #pragma unroll
-        for (int m = 0; m < MF; ++m)
+        for (int m = 0; m < MF; ++m) {
             for (int off = 32; off >= 1; off >>= 1)
                 acc[m] += __shfl_xor(acc[m], off);
+            const float t = isd ? acc[m] : acc[m] * a.h.sb[c];
+            hi[m] = f32_to_bf16_rne(t);
+            lo[m] = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi[m] << 16));
+        }
+    };
+    // publish column i to the workspace: device-scope stores, completed
+    // before the column's flag is set to the call's tag (no cache write-back
+    // needed: they went to the device's coherence point)
+    auto publish = [&](int i) __attribute__((always_inline)) {
+        uint16_t hi[MF], lo[MF];
+        column(i, hi, lo);
+        const bool isd = i >= k;
+        const int64_t c = isd ? i - k : i;
         const int64_t Mp = a.w.Mp;
 #pragma unroll
         for (int m = 0; m < MF; ++m)
             if (lane == m) {
-                const float t = isd ? acc[m] : acc[m] * a.h.sb[c];
-                const uint16_t hi = f32_to_bf16_rne(t);
-                const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
-                uint16_t *ph = isd ? a.w.s16 + m * rpad + c : a.w.t16 + m * kpad + c;
-                uint16_t *pl = isd ? a.w.s16 + (Mp + m) * rpad + c : a.w.t16 + (Mp + m) * kpad + c;
-                store_device(ph, hi);
-                store_device(pl, lo);
+                store_device(isd ? a.w.s16 + m * rpad + c : a.w.t16 + m * kpad + c, hi[m]);
+                store_device(isd ? a.w.s16 + (Mp + m) * rpad + c : a.w.t16 + (Mp + m) * kpad + c, lo[m]);
             }
-        // publish: the device-scope stores have completed before the count
-        // goes up (no cache write-back needed: they went to the device's
-        // coherence point)
         wait_vm_all();
-        if (lane == 0)
-            __hip_atomic_fetch_add(finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            __hip_atomic_store(a.w.colflag + i, __builtin_amdgcn_readfirstlane(epoch) + 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(sync + sync_published(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     };
 
     // wave-level direct-to-LDS copy of n16 16-byte pieces, read at device
@@ -241,6 +248,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                                                  kDmaDevice);
         }
     };
+    // t and s of the MF rows into this wave's LDS region, copied from the
+    // workspace once every column is published (nothing in this kernel ever
+    // waits for another wave)
     auto stage_ts = [&]() __attribute__((always_inline)) {
         const int64_t Mp = a.w.Mp;
         wave_dma16(a.w.t16, s_ts, MF * kpad / 8);
@@ -248,37 +258,70 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         wave_dma16(a.w.s16, s_ts + 2 * MF * kpad, MF * rpad / 8);
         wave_dma16(a.w.s16 + Mp * rpad, s_ts + 2 * MF * kpad + MF * rpad, MF * rpad / 8);
     };
-    // t and s of the MF rows into this wave's LDS region once every column
-    // is published.  A wave that finds columns missing first claims and
-    // computes every column still unclaimed, so it waits only for columns
-    // held by running waves, which compute them without waiting; the wait
-    // is bounded all the same (about 2^20 x 128 clocks), so that a launch
-    // always ends even if the counters were left inconsistent (the logits
-    // would then be wrong).
-    auto wait_and_stage_ts = [&]() __attribute__((always_inline)) {
-        const uint32_t need = (uint32_t)ntask;
-        if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-            for (int g = 0; g < kSyncGroups; ++g)
-                for (;;) {
-                    const int t = claim(g);
-                    if (t >= group_size(g))
-                        break;
-                    run_task(g + kSyncGroups * t);
+    // Fallback when the count fell short: build t and s in LDS column by
+    // column.  A column whose flag carries this call's tag is read from the
+    // workspace after the flag (its values were complete before the flag
+    // was set); every other column the wave computes itself.
+    auto build_ts = [&]() __attribute__((always_inline)) {
+        uint32_t *r = (uint32_t *)s_ts; // padding columns must read as 0
+        const int64_t nw32 = MF * (kpad + rpad); // 2 * MF * (kpad + rpad) bf16
+        for (int64_t i = lane; i < nw32; i += 64)
+            r[i] = 0u;
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(epoch) + 1u;
+        const int64_t Mp = a.w.Mp;
+        for (int q = 0; q * 64 < ntask; ++q) {
+            const int i = q * 64 + lane;
+            const bool valid = i < ntask;
+            const uint32_t f =
+                __hip_atomic_load(a.w.colflag + (valid ? i : ntask - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool pub = valid && f == tag;
+            if (pub) {
+                const bool isd = i >= k;
+                const int64_t c = isd ? i - k : i;
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    const uint16_t hi = __hip_atomic_load(isd ? a.w.s16 + m * rpad + c : a.w.t16 + m * kpad + c,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint16_t lo =
+                        __hip_atomic_load(isd ? a.w.s16 + (Mp + m) * rpad + c : a.w.t16 + (Mp + m) * kpad + c,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (isd) {
+                        s_ts[2 * MF * kpad + m * rpad + c] = hi;
+                        s_ts[2 * MF * kpad + (MF + m) * rpad + c] = lo;
+                    } else {
+                        s_ts[m * kpad + c] = hi;
+                        s_ts[(MF + m) * kpad + c] = lo;
+                    }
                 }
-            for (int spin = 0; spin < (1 << 20); ++spin) {
-                if (__hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
-                    break;
-                __builtin_amdgcn_s_sleep(2);
+            }
+            uint64_t miss = __ballot(valid && !pub);
+            while (miss) {
+                const int j = q * 64 + __builtin_ctzll(miss);
+                miss &= miss - 1;
+                uint16_t hi[MF], lo[MF];
+                column(j, hi, lo);
+                const bool isd = j >= k;
+                const int64_t c = isd ? j - k : j;
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+                    if (lane == m) {
+                        if (isd) {
+                            s_ts[2 * MF * kpad + m * rpad + c] = hi[m];
+                            s_ts[2 * MF * kpad + (MF + m) * rpad + c] = lo[m];
+                        } else {
+                            s_ts[m * kpad + c] = hi[m];
+                            s_ts[(MF + m) * kpad + c] = lo[m];
+                        }
+                    }
             }
         }
-        stage_ts();
     };
 
     // ---- the chunk stream, in pairs of chunks ----
     const int64_t nrp = nkc / 2, nlp = nlr / 2;                  // both even
     // residual pairs before the low-rank ones (even; with no low-rank
     // chunks, all but the last two)
-    const int64_t nrp1 = nlr > 0 ? ((nrp / 2) & ~int64_t(1)) : nrp - 2;
+    const int64_t nrp1 = nlr > 0 ? ((3 * nrp / 4) & ~int64_t(1)) : nrp - 2;
     const int64_t c1 = 2 * nrp1, c2 = c1 + nlr, npairs = nrp + nlp;
     const u32x4 *lrp = (const u32x4 *)a.h.lr;
     const u32x4 *r4p = (const u32x4 *)a.h.r4;
@@ -295,13 +338,97 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         load_chunk(p.h1, 2 * pi + 1);
     };
 
-    // projection columns: wave gw owns the indices i = gw, gw + nw, ... below
-    // k + r (nw waves in the grid) and takes one ticket of group i % 16 for
-    // each, so the grid's tickets at its start cover every column exactly
-    // once.  The first ticket is requested before anything else.
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wv, nw = (int64_t)a.nwg * 4;
-    const int g0 = (int)(gw % kSyncGroups);
-    const int t0 = gw < ntask ? claim(g0) : 0;
+    // Projection columns.  With projection-only workgroups, their wave pw
+    // publishes columns pw, pw + 4 ntwg, ...; they start at once, stream
+    // nothing and leave.  Without them, streaming wave gw publishes columns
+    // gw, gw + nw, ... (nw streaming waves) before its residual.
+    if (proj_wg) {
+        const int64_t nx = MF * d / 8;
+        for (int64_t i0 = 0; i0 < nx; i0 += 256) {
+            const int64_t i = i0 + threadIdx.x;
+            if (i < nx)
+                __builtin_amdgcn_global_load_lds((const void *)((const u32x4 *)a.X + i),
+                                                 (__attribute__((address_space(3))) void *)((u32x4 *)(smem + a.lds_x) + i0 + wv * 64), 16, 0, 0);
+        }
+        __syncthreads();
+        // up to PB columns per batch, all their loads issued together, one
+        // wait for all their stores: under the full memory load of the
+        // streaming workgroups every round trip is long
+        constexpr int PB = MF == 1 ? 4 : 2;
+        const int64_t stride = (int64_t)a.ntwg * 4;
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(epoch) + 1u;
+        const int64_t Mp = a.w.Mp;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int64_t i0 = (int64_t)blockIdx.x * 4 + wv; i0 < ntask; i0 += PB * stride) {
+            int ci[PB];
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+                const int64_t i = i0 + b * stride;
+                ci[b] = (int)(i < ntask ? i : ntask - 1); // past the end: repeat the last column
+            }
+            float acc[PB][MF];
+#pragma unroll
+            for (int b = 0; b < PB; ++b)
+#pragma unroll
+                for (int m = 0; m < MF; ++m)
+                    acc[b][m] = 0.f;
+            for (int64_t j00 = 0; j00 < d; j00 += 4096) {
+                u32x4 wq[PB][4];
+                float sc[PB][4];
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+                    const bool isd = ci[b] >= k;
+                    const int64_t c = isd ? ci[b] - k : ci[b];
+                    const int8_t *row = isd ? a.h.d8 + c * d : a.h.b8 + c * d;
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int64_t j0 = j00 + 1024 * it + 16 * lane;
+                        const int64_t jc = j0 < d ? j0 : 0;
+                        wq[b][it] = *(const u32x4 *)(row + jc);
+                        sc[b][it] = isd ? a.h.sd[c * G + jc / a.h.s.g] : 1.0f;
+                    }
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int64_t j0 = j00 + 1024 * it + 16 * lane;
+                    const bool ok = j0 < d;
+#pragma unroll
+                    for (int m = 0; m < MF; ++m) {
+                        const u32x4 *xp = (const u32x4 *)(s_x + m * d + (ok ? j0 : 0));
+                        const u32x4 x0 = ok ? xp[0] : z, x1 = ok ? xp[1] : z;
+#pragma unroll
+                        for (int b = 0; b < PB; ++b)
+                            acc[b][m] = __builtin_fmaf(sc[b][it], dot16(ok ? wq[b][it] : z, x0, x1), acc[b][m]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+                const bool isd = ci[b] >= k;
+                const int64_t c = isd ? ci[b] - k : ci[b];
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    float v = acc[b][m];
+                    for (int off = 32; off >= 1; off >>= 1)
+                        v += __shfl_xor(v, off);
+                    const float t = isd ? v : v * a.h.sb[c];
+                    const uint16_t hi = f32_to_bf16_rne(t);
+                    const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
+                    if (lane == m && i0 + b * stride < ntask) {
+                        store_device(isd ? a.w.s16 + m * rpad + c : a.w.t16 + m * kpad + c, hi);
+                        store_device(isd ? a.w.s16 + (Mp + m) * rpad + c : a.w.t16 + (Mp + m) * kpad + c, lo);
+                    }
+                }
+            }
+            wait_vm_all();
+            if (lane < PB && i0 + lane * stride < ntask) {
+                __hip_atomic_store(a.w.colflag + i0 + lane * stride, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(sync + sync_published(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        return;
+    }
+    const int64_t gw = bid * 4 + wv, nw = (int64_t)a.nwg * 4;
 
     DPair<NV> P0, P1;
     load_pair(P0, 0);
@@ -323,18 +450,11 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         }
     }
     __syncthreads();
-    if (gw < ntask) {
-        if (t0 < group_size(g0))
-            run_task(g0 + kSyncGroups * t0);
-        for (int64_t i = gw + nw; i < ntask; i += nw) {
-            const int g = (int)(i % kSyncGroups);
-            const int t = claim(g);
-            if (t < group_size(g))
-                run_task(g + kSyncGroups * t);
-        }
-    }
+    if (a.ntwg == 0)
+        for (int64_t i = gw; i < ntask; i += nw)
+            publish((int)i);
 
-    // per-lane partial sums over the lane's columns
+    // VALU variant: per-lane partial sums over the lane's columns
     float tot[NV][MF], g[NV][MF], xn[MF];
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
@@ -343,12 +463,68 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         for (int v = 0; v < NV; ++v)
             tot[v][m] = g[v][m] = 0.f;
     }
+    // matrix-core variant: [16 rows of X (row m in lanes 16(m/4)..) x 16
+    // vocabulary rows] tiles; lane l holds rows 4(l/16) + i of column l % 16.
+    // Chunk kc accumulates into gq[kc & 1] and is folded one chunk later
+    // (reading an accumulator right after its MFMAs would stall the wave).
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NV], gq[2][NV], nx[2];
+    bool pend = false; // chunk kc - 1 still to fold
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        acc[v] = zero4;
+    const int64_t xrow = lr < MF ? lr : MF - 1; // A-operand rows past M repeat the last row
     const uint32_t kMagic = vgpr_const(kBf16Magic);
     const uint32_t c136 = vgpr_const(kBf16Neg136), c144 = vgpr_const(kBf16Neg144);
+    const u32x4 c136x4 = {c136, c136, c136, c136}, c144x4 = {c144, c144, c144, c144};
+
+    auto fold_mx = [&](int sel, int64_t kc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const float scl = h2f(s_sr[((wv * NV + v) * G + kc) * kVB + lr]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[v][i] = __builtin_fmaf(scl, gq[sel][v][i] + nx[sel][i], acc[v][i]);
+        }
+    };
+    auto flush_mx = [&](int64_t kc_last) __attribute__((always_inline)) {
+        // (constant accumulator indices only: a run-time index would put the
+        // accumulators in scratch memory)
+        if (MX && pend) {
+            if (kc_last & 1)
+                fold_mx(1, kc_last);
+            else
+                fold_mx(0, kc_last);
+        }
+        pend = false;
+    };
 
     // residual K-chunk kc: 4 K-steps; each g-group is folded with its scale
     // when it ends: tot += sR (sum x (q + 136) - 136 sum x)
-    auto res_chunk = [&](const DChunk<NV> &c, int64_t kc) __attribute__((always_inline)) {
+    auto res_chunk = [&](const DChunk<NV> &c, int64_t kc, int sel) __attribute__((always_inline)) {
+        if constexpr (MX) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int64_t ks = kc * 4 + s;
+                const u32x4 xa = *(const u32x4 *)(s_x + xrow * d + ks * kKStep + 8 * lq);
+                nx[sel] = mfma_bf16(xa, c136x4, s == 0 ? zero4 : nx[sel]);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const uint32_t wd = s == 0 ? c.q[v].x : s == 1 ? c.q[v].y : s == 2 ? c.q[v].z : c.q[v].w;
+                    gq[sel][v] = mfma_bf16(xa, r4_bf16(wd, kMagic), s == 0 ? zero4 : gq[sel][v]);
+                }
+                pin4(nx[sel]);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    pin4(gq[sel][v]);
+                step_fence();
+            }
+            if (pend)
+                fold_mx(sel ^ 1, kc - 1);
+            pend = true;
+            step_fence();
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int64_t ks = kc * 4 + s;
@@ -398,8 +574,55 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // low-rank chunk j: three core K-steps (A5 + 16 against t) or two
     // correction K-steps (C8 against s); K-steps beyond the rank are skipped
     float ga[NV][MF], gc[NV][MF], nt[MF];
+    f32x4 gam[NV], gcm[NV], ntm;
     const uint16_t *s_t = s_ts, *s_s = s_ts + 2 * MF * kpad;
     auto lr_chunk = [&](const DChunk<NV> &c, int64_t j) __attribute__((always_inline)) {
+        if constexpr (MX) {
+            if (j < na) {
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const int64_t ks = 3 * j + q;
+                    if (ks >= kst)
+                        break;
+                    const u32x4 th = *(const u32x4 *)(s_t + xrow * kpad + ks * kKStep + 8 * lq);
+                    const u32x4 tl = *(const u32x4 *)(s_t + (MF + xrow) * kpad + ks * kKStep + 8 * lq);
+                    ntm = mfma_bf16(tl, c144x4, mfma_bf16(th, c144x4, ntm));
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        const uint32_t wn = q == 0 ? c.q[v].x : q == 1 ? c.q[v].y : c.q[v].z;
+                        const u32x4 b = a5_bf16_q(wn, c.q[v].w, q);
+                        gam[v] = mfma_bf16(tl, b, mfma_bf16(th, b, gam[v]));
+                    }
+                    pin4(ntm);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        pin4(gam[v]);
+                    step_fence();
+                }
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int64_t ks = 2 * (j - na) + hh;
+                    if (ks >= rst)
+                        break;
+                    const u32x4 sh = *(const u32x4 *)(s_s + xrow * rpad + ks * kKStep + 8 * lq);
+                    const u32x4 sl = *(const u32x4 *)(s_s + (MF + xrow) * rpad + ks * kKStep + 8 * lq);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        u32x2 w;
+                        w.x = hh == 0 ? c.q[v].x : c.q[v].z;
+                        w.y = hh == 0 ? c.q[v].y : c.q[v].w;
+                        const u32x4 b = c8_bf16(w);
+                        gcm[v] = mfma_bf16(sl, b, mfma_bf16(sh, b, gcm[v]));
+                    }
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+                        pin4(gcm[v]);
+                    step_fence();
+                }
+            }
+            return;
+        }
         if (j < na) {
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
@@ -466,14 +689,14 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // kc0 + 3) or low-rank pairs pi, pi + 1; the last iteration issues no
     // loads (no load sits under a branch, which would make the compiler copy
     // the prefetch buffers)
-    auto res_iter = [&](int64_t pi, int64_t kc0, bool load) __attribute__((always_inline)) {
-        res_chunk(P0.h0, kc0);
-        res_chunk(P0.h1, kc0 + 1);
+    auto res_iter = [&](int64_t pi, int64_t kc0, bool load) __attribute__((always_inline)) { // kc0 % 4 == 0
+        res_chunk(P0.h0, kc0, 0);
+        res_chunk(P0.h1, kc0 + 1, 1);
         if (load)
             load_pair(P0, pi + 2);
         __builtin_amdgcn_sched_barrier(0);
-        res_chunk(P1.h0, kc0 + 2);
-        res_chunk(P1.h1, kc0 + 3);
+        res_chunk(P1.h0, kc0 + 2, 0);
+        res_chunk(P1.h1, kc0 + 3, 1);
         if (load)
             load_pair(P1, pi + 3);
         __builtin_amdgcn_sched_barrier(0);
@@ -491,26 +714,33 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 
     // One control path for every shape (separate paths for the cases made
     // the register allocator spill the prefetch buffers).  The last
-    // iteration before the low-rank pairs reads the published-column count,
-    // issued ahead of the iteration's prefetch so that waiting for it costs
-    // nothing (loads complete in order).  If it shows every column, t and s
-    // are copied to LDS with no further wait (a copy issued inside the loops
-    // would cost registers).
+    // iteration before the low-rank pairs reads the count of published
+    // columns, issued ahead of the iteration's prefetch so that waiting for
+    // it costs nothing (loads complete in order).  The count grows by k + r
+    // per call and is never reset, so it equals (k + r)(calls before + 1)
+    // exactly when this call has published every column.  t and s are then
+    // copied to LDS (a copy issued inside the loops would cost registers);
+    // if the count fell short, the column flags tell which columns the wave
+    // must compute itself.
     int64_t pi = 0;
     for (; pi + 2 < nrp1; pi += 2)
         res_iter(pi, 2 * pi, true);
-    bool ready = false;
+    uint32_t seen = 0;
     if (nrp1 >= 2) {
-        const uint32_t seen = __hip_atomic_load(finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        seen = __hip_atomic_load(sync + sync_published(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         res_iter(pi, 2 * pi, true);
         pi += 2;
-        ready = __builtin_amdgcn_readfirstlane(seen) >= (uint32_t)ntask;
     }
+    flush_mx(2 * pi - 1);
     if (nlr > 0) {
-        if (ready)
+        const bool ready = nrp1 >= 2 && __builtin_amdgcn_readfirstlane(seen) ==
+                                            (uint32_t)ntask * (__builtin_amdgcn_readfirstlane(epoch) + 1u);
+        if (ready) {
             stage_ts();
-        else
-            wait_and_stage_ts();
+            wait_vm_all(); // the copy has landed
+        } else {
+            build_ts();
+        }
     }
     // row scales of the low-rank terms, consumed after the low-rank pairs
     float sa[NV], sc[NV];
@@ -519,10 +749,6 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         sa[v] = h2f(a.h.sa[vb[v] * kVB + lr]);
         sc[v] = h2f(a.h.sc[vb[v] * kVB + lr]);
     }
-    // the copies of t and s must have landed before the first LDS read of
-    // them (the compiler's own tracking of direct-to-LDS copies does not
-    // cover every read of the region)
-    wait_vm_all();
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
         nt[m] = 0.f;
@@ -530,18 +756,30 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         for (int v = 0; v < NV; ++v)
             ga[v][m] = gc[v][m] = 0.f;
     }
+    ntm = zero4;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        gam[v] = gcm[v] = zero4;
     // at least two residual pairs follow, so every iteration prefetches
     for (; pi < nrp1 + nlp; pi += 2)
         lr_iter(pi);
-    // tot += sA (A5 t - 144 sum t) + sC (C8 s), per lane
+    // tot += sA (A5 t - 144 sum t) + sC (C8 s)
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v) {
+        if constexpr (MX) {
 #pragma unroll
-        for (int m = 0; m < MF; ++m)
-            tot[v][m] = __builtin_fmaf(sa[v], ga[v][m] + nt[m], __builtin_fmaf(sc[v], gc[v][m], tot[v][m]));
+            for (int i = 0; i < 4; ++i)
+                acc[v][i] = __builtin_fmaf(sa[v], gam[v][i] + ntm[i], __builtin_fmaf(sc[v], gcm[v][i], acc[v][i]));
+        } else {
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                tot[v][m] = __builtin_fmaf(sa[v], ga[v][m] + nt[m], __builtin_fmaf(sc[v], gc[v][m], tot[v][m]));
+        }
+    }
     for (; pi + 2 < npairs; pi += 2)
         res_iter(pi, 2 * pi - nlr, true);
     res_iter(pi, 2 * pi - nlr, false);
+    flush_mx(nkc - 1);
 
     // ---- logits: the four lanes of a row add their partial sums ----
     uint64_t key[MF];
@@ -554,9 +792,14 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
-            float y = tot[v][m];
-            y += __shfl_xor(y, 16);
-            y += __shfl_xor(y, 32);
+            float y;
+            if constexpr (MX) {
+                y = acc[v][m]; // row m of lanes 0..15 (MF <= 4)
+            } else {
+                y = tot[v][m];
+                y += __shfl_xor(y, 16);
+                y += __shfl_xor(y, 32);
+            }
             yv[v][m] = y;
             if (row < V)
                 key[m] = umax64(key[m], argmax_key(y, (uint32_t)row));
@@ -591,9 +834,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 red[wv][m] = kk;
         }
     }
-    // every wave of the workgroup is past its last use of the counters (and
-    // has its keys in LDS); no stores are outstanding yet, so the barrier's
-    // wait for memory is short
+    // every wave of the workgroup is past its last use of the counters and
+    // has its keys in LDS
     __syncthreads();
     if (wv != 0) {
         store_logits();
@@ -602,7 +844,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // wave 0.  Device-scope atomics are performed at the device's coherence
     // point; each is complete before the count that follows it.
     const int nslot = a.nwg < kSyncGroups ? a.nwg : kSyncGroups;
-    const int slot = (int)(blockIdx.x % nslot);
+    const int slot = (int)(bid % nslot);
     const uint32_t slot_size = (uint32_t)((a.nwg - 1 - slot) / nslot + 1);
     uint64_t *const slot_key = a.w.keys + slot * 32, *const top_key = a.w.keys + kSyncGroups * 32;
     if (a.argmax && lane < MF) {
@@ -631,11 +873,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     __hip_atomic_exchange(top_key + lane, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
             }
-            if (lane < kSyncGroups)
-                __hip_atomic_store(sync + sync_claimed(lane), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (lane == 0) {
-                __hip_atomic_store(finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(sync + sync_epoch(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -661,30 +901,54 @@ static DecodeLds decode_lds(const Shape &s, int64_t M)
     return L;
 }
 
-bool gemv_decode_ok(const DevHead &h, int64_t M)
+typedef void (*DecodeKernel)(DecodeArgs);
+
+template <DecodeKernel K>
+static bool scratch_free() // asked once per instance
+{
+    static const bool ok = [] {
+        hipFuncAttributes fa;
+        return hipFuncGetAttributes(&fa, (const void *)K) == hipSuccess && fa.localSizeBytes == 0;
+    }();
+    return ok;
+}
+
+// The kernel instance for (M, g, mx), or null when the shape is outside the
+// single-launch path.  Instances are used only where they were compiled
+// without scratch (private) memory: their timing assumes no spill traffic
+// on the vector-memory counter, and the larger-M instances that would need
+// it are not offered.
+static DecodeKernel decode_kernel(const DevHead &h, int64_t M, bool mx)
 {
     // residual pairs and low-rank pairs each come in even counts (n_lr is a
-    // multiple of 4 by construction)
-    return M >= 1 && M <= kDecodeMaxM && h.s.nkc() % 4 == 0 && decode_lds(h.s, M).total <= 159 * 1024;
-}
-
-template <int MF>
-static hipError_t launch_mf(const DecodeArgs &a, size_t lds, hipStream_t st)
-{
-    auto kern = a.gsteps == 4 ? gemv_decode_kernel<MF, 4> : gemv_decode_kernel<MF, 0>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
+    // multiple of 4 by construction); the matrix-core variant folds one
+    // g = 128 group per K-chunk
+    if (M < 1 || M > kDecodeMaxM || h.s.nkc() % 4 != 0 || decode_lds(h.s, M).total > 159 * 1024)
+        return nullptr;
+    const bool g128 = h.s.g == 4 * kKStep;
+    if (mx) {
+        if (g128 && M == 1 && scratch_free<gemv_decode_kernel<1, 4, true>>())
+            return gemv_decode_kernel<1, 4, true>;
+        return nullptr;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.nwg), dim3(256), lds, st, a);
-    return hipGetLastError();
+    if (M == 1) {
+        if (g128)
+            return scratch_free<gemv_decode_kernel<1, 4, false>>() ? gemv_decode_kernel<1, 4, false> : nullptr;
+        return scratch_free<gemv_decode_kernel<1, 0, false>>() ? gemv_decode_kernel<1, 0, false> : nullptr;
+    }
+    // M = 2 only with g = 128 (the general-g instance needs scratch memory)
+    if (g128)
+        return scratch_free<gemv_decode_kernel<2, 4, false>>() ? gemv_decode_kernel<2, 4, false> : nullptr;
+    return nullptr;
 }
 
-hipError_t launch_gemv_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                              int32_t *argmax, hipStream_t st)
+bool decode_ok(const DevHead &h, int64_t M, bool mx) { return decode_kernel(h, M, mx) != nullptr; }
+
+hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
+                         bool mx, hipStream_t st)
 {
-    if (!gemv_decode_ok(h, w.M))
+    const DecodeKernel kern = decode_kernel(h, w.M, mx);
+    if (!kern)
         return hipErrorInvalidValue;
     const DecodeLds L = decode_lds(h.s, w.M);
     DecodeArgs a;
@@ -702,14 +966,19 @@ hipError_t launch_gemv_decode(const DevHead &h, const Work &w, const uint16_t *X
     a.ntask = (int)(h.s.k + h.s.r);
     const int nv = decode_nv((int)w.M);
     a.nwg = (int)((a.nvb + 4 * nv - 1) / (4 * nv));
+    // projection-only workgroups take the slots the streaming ones leave
+    // free (two workgroups per CU), at least one column per wave
+    const int64_t spare = int64_t(2) * h.n_cu - a.nwg;
+    a.ntwg = spare > 0 ? (int)std::min<int64_t>(spare, (a.ntask + 3) / 4) : 0;
     a.lds_x = L.x;
     a.lds_ts = L.ts;
-    switch (w.M) {
-    case 1: return launch_mf<1>(a, L.total, st);
-    case 2: return launch_mf<2>(a, L.total, st);
-    case 3: return launch_mf<3>(a, L.total, st);
-    default: return launch_mf<4>(a, L.total, st);
+    if (L.total > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+        if (e != hipSuccess)
+            return e;
     }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.ntwg + a.nwg)), dim3(256), L.total, st, a);
+    return hipGetLastError();
 }
 
 } // namespace archead

@@ -41,13 +41,15 @@ int64_t lds_max_n_part(const Shape &s);
 // smallest M for which the automatic choice takes a2-L
 constexpr int64_t kLdsMinM = 128;
 
-// a1 + a2-G + a3 in one launch for M <= kDecodeMaxM: VALU bf16-pair dot
-// products, the projection columns computed by the grid's first waves, the
-// argmax resolved by the last workgroup.  gemv_decode_ok tells whether a
-// shape and M are supported.
-bool gemv_decode_ok(const DevHead &h, int64_t M);
-hipError_t launch_gemv_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
-                              int32_t *argmax, hipStream_t st);
+// a1 + a2 + a3 in one launch for M <= kDecodeMaxM: the projection columns
+// computed by the grid's first waves, the argmax resolved by the last
+// workgroup.  mx = false: VALU bf16-pair dot products (a2-G); mx = true:
+// the same stream with the products on the matrix cores (a2-S, g = 128,
+// M = 1).
+// decode_ok tells whether a shape and M are supported.
+bool decode_ok(const DevHead &h, int64_t M, bool mx);
+hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
+                         bool mx, hipStream_t st);
 
 // a3: reduce the argmax partial keys of each row to an index.
 hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st);

@@ -124,27 +124,29 @@ struct Work {
     // below), all zero between calls (the launch puts them back to zero)
     uint32_t *sync;    // [kSyncWords]
     uint64_t *keys;    // [kKeyWords]
+    uint32_t *colflag; // [k + r] call number + 1 once column i of t / s is published
 };
 
-constexpr int kDecodeMaxM = 4; // largest M of the single-launch decode path
+constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path
 
 // Work counters of the single-launch decode path.  Atomics on one address
 // serialise (about 10 ns each), so counters that many workgroups update are
 // split into kSyncGroups copies, each in its own 256-byte line:
-//   claimed[g]    projection columns of group g claimed so far
+//   (line g < kSyncGroups: unused)
 //   slot_done[s]  workgroups of slot s finished
-//   finished      projection columns published
+//   epoch         calls completed (never reset; tags the column flags)
 //   top_done      slots finished
+//   published     projection columns published (never reset: k + r per call)
 // and the argmax keys: per slot s, keys[s * 32 + m]; the grid's,
 // keys[kSyncGroups * 32 + m], m < kDecodeMaxM.
 constexpr int kSyncGroups = 16;
 constexpr int kSyncStride = 64; // uint32 per 256-byte line
-constexpr size_t kSyncWords = size_t(2 * kSyncGroups + 2) * kSyncStride;
+constexpr size_t kSyncWords = size_t(2 * kSyncGroups + 3) * kSyncStride;
 constexpr size_t kKeyWords = size_t(kSyncGroups + 1) * 32;
-__host__ __device__ constexpr size_t sync_claimed(int g) { return size_t(g) * kSyncStride; }
 __host__ __device__ constexpr size_t sync_slot_done(int s) { return size_t(kSyncGroups + s) * kSyncStride; }
-__host__ __device__ constexpr size_t sync_finished() { return size_t(2 * kSyncGroups) * kSyncStride; }
+__host__ __device__ constexpr size_t sync_epoch() { return size_t(2 * kSyncGroups) * kSyncStride; }
 __host__ __device__ constexpr size_t sync_top_done() { return size_t(2 * kSyncGroups + 1) * kSyncStride; }
+__host__ __device__ constexpr size_t sync_published() { return size_t(2 * kSyncGroups + 2) * kSyncStride; }
 
 // Host relayout (pack.cpp).  Inputs in the canonical host layout; outputs are
 // host buffers in the device layout, sized by Shape::n_*.
