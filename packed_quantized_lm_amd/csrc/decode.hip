@@ -467,12 +467,17 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // vocabulary rows] tiles; lane l holds rows 4(l/16) + i of column l % 16.
     // Chunk kc accumulates into gq[kc & 1] and is folded one chunk later
     // (reading an accumulator right after its MFMAs would stall the wave).
+    // Only rows m < MF of the tiles are kept in the running totals (lanes
+    // 0..15 hold them, MF <= 4).
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[NV], gq[2][NV], nx[2];
+    f32x4 gq[2][NV], nx[2];
+    float acc[NV][MF];
     bool pend = false; // chunk kc - 1 still to fold
 #pragma unroll
     for (int v = 0; v < NV; ++v)
-        acc[v] = zero4;
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+            acc[v][m] = 0.f;
     const int64_t xrow = lr < MF ? lr : MF - 1; // A-operand rows past M repeat the last row
     const uint32_t kMagic = vgpr_const(kBf16Magic);
     const uint32_t c136 = vgpr_const(kBf16Neg136), c144 = vgpr_const(kBf16Neg144);
@@ -483,8 +488,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         for (int v = 0; v < NV; ++v) {
             const float scl = h2f(s_sr[((wv * NV + v) * G + kc) * kVB + lr]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[v][i] = __builtin_fmaf(scl, gq[sel][v][i] + nx[sel][i], acc[v][i]);
+            for (int m = 0; m < MF; ++m)
+                acc[v][m] = __builtin_fmaf(scl, gq[sel][v][m] + nx[sel][m], acc[v][m]);
         }
     };
     auto flush_mx = [&](int64_t kc_last) __attribute__((always_inline)) {
@@ -690,25 +695,37 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // loads (no load sits under a branch, which would make the compiler copy
     // the prefetch buffers)
     auto res_iter = [&](int64_t pi, int64_t kc0, bool load) __attribute__((always_inline)) { // kc0 % 4 == 0
+        // each chunk's registers are refilled as soon as the chunk is used,
+        // so that close to four chunks stay in flight
         res_chunk(P0.h0, kc0, 0);
+        if (load)
+            load_chunk(P0.h0, 2 * pi + 4);
+        __builtin_amdgcn_sched_barrier(0);
         res_chunk(P0.h1, kc0 + 1, 1);
         if (load)
-            load_pair(P0, pi + 2);
+            load_chunk(P0.h1, 2 * pi + 5);
         __builtin_amdgcn_sched_barrier(0);
         res_chunk(P1.h0, kc0 + 2, 0);
+        if (load)
+            load_chunk(P1.h0, 2 * pi + 6);
+        __builtin_amdgcn_sched_barrier(0);
         res_chunk(P1.h1, kc0 + 3, 1);
         if (load)
-            load_pair(P1, pi + 3);
+            load_chunk(P1.h1, 2 * pi + 7);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto lr_iter = [&](int64_t pi) __attribute__((always_inline)) {
         lr_chunk(P0.h0, 2 * pi - c1);
+        load_chunk(P0.h0, 2 * pi + 4);
+        __builtin_amdgcn_sched_barrier(0);
         lr_chunk(P0.h1, 2 * pi + 1 - c1);
-        load_pair(P0, pi + 2);
+        load_chunk(P0.h1, 2 * pi + 5);
         __builtin_amdgcn_sched_barrier(0);
         lr_chunk(P1.h0, 2 * pi + 2 - c1);
+        load_chunk(P1.h0, 2 * pi + 6);
+        __builtin_amdgcn_sched_barrier(0);
         lr_chunk(P1.h1, 2 * pi + 3 - c1);
-        load_pair(P1, pi + 3);
+        load_chunk(P1.h1, 2 * pi + 7);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -768,8 +785,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     for (int v = 0; v < NV; ++v) {
         if constexpr (MX) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[v][i] = __builtin_fmaf(sa[v], gam[v][i] + ntm[i], __builtin_fmaf(sc[v], gcm[v][i], acc[v][i]));
+            for (int m = 0; m < MF; ++m)
+                acc[v][m] = __builtin_fmaf(sa[v], gam[v][m] + ntm[m], __builtin_fmaf(sc[v], gcm[v][m], acc[v][m]));
         } else {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
