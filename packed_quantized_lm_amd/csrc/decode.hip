@@ -76,7 +76,39 @@ __device__ __forceinline__ void store_device(uint16_t *p, uint16_t v)
 // atomics included, has completed
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-constexpr int kDmaDevice = 16; // cache-policy operand of global_load_lds: sc1, device scope
+// s_waitcnt operand for vmcnt(n) alone (n < 64; low four bits at 3:0, high
+// two at 15:14; expcnt and lgkmcnt at their no-wait maxima)
+constexpr unsigned waitcnt_vm(unsigned n) { return (n & 15u) | ((n >> 4) & 3u) << 14 | 0x7u << 4 | 0xFu << 8; }
+static_assert(waitcnt_vm(0) == 0x0F70u, "vmcnt(0)");
+
+// Direct copy of one 16-byte piece per lane from global memory (p, per
+// lane) to LDS (dst + 16 lane; dst the same in every lane), sc1 (device
+// scope) when DEVICE.  Written as inline assembly because its callers wait
+// for the copy themselves with a partial vmcnt: the compiler, which cannot
+// tell which LDS reads a copy may alias, would wait for every outstanding
+// load (vmcnt(0)) before the next LDS read or barrier.  Hidden from the
+// compiler's count of outstanding loads, the copy can only make its waits
+// stricter than needed, never too weak.  M0 (the LDS base of the copy) is
+// restored afterwards.
+template <bool DEVICE>
+__device__ __forceinline__ void lds_dma16(const void *p, void *dst)
+{
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+    uint32_t m0;
+    if constexpr (DEVICE)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off sc1\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                     : "=&s"(m0)
+                     : "v"(p), "s"(base)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                     : "=&s"(m0)
+                     : "v"(p), "s"(base)
+                     : "memory");
+}
 
 // Keeps one K-step's loads and arithmetic together: no memory access moves
 // across it in the optimiser (empty asm with a memory clobber) or in the
@@ -108,7 +140,7 @@ struct DecodeArgs {
     int ntwg;        // projection-only workgroups, first in the grid (0: the
                      // streaming waves compute the columns themselves)
     int nwg;         // streaming workgroups, after them
-    unsigned lds_x, lds_ts; // byte offsets of the X and t/s regions (sr at 0)
+    unsigned lds_sa, lds_x, lds_ts; // byte offsets of the sA/sC, X and t/s regions (sr at 0)
 };
 
 // v-blocks per wave: five at M = 1, four at M = 2 (whose accumulators need
@@ -127,6 +159,7 @@ struct DPair {
 
 // LDS of one workgroup:
 //   sr  [4*NV][G][16]        fp16  residual scales of its v-blocks
+//   sa  [2][4*NV][16]        fp16  sA, then sC, of its rows
 //   x   [MF][d]              bf16  the hidden states
 //   ts  [4 waves] x { t hi [MF][kpad], t lo [MF][kpad], s hi [MF][rpad], s lo [MF][rpad] }  bf16
 //
@@ -237,15 +270,14 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         }
     };
 
-    // wave-level direct-to-LDS copy of n16 16-byte pieces, read at device
-    // scope (the data were written by other workgroups of this launch)
+    // wave-level copy of n16 16-byte pieces from the workspace to LDS, read
+    // at device scope (the data were written by other workgroups of this
+    // launch)
     auto wave_dma16 = [&](const void *src, void *dst, int64_t n16) __attribute__((always_inline)) {
         for (int64_t i0 = 0; i0 < n16; i0 += 64) {
             const int64_t i = i0 + lane;
             if (i < n16)
-                __builtin_amdgcn_global_load_lds((const void *)((const u32x4 *)src + i),
-                                                 (__attribute__((address_space(3))) void *)((u32x4 *)dst + i0), 16, 0,
-                                                 kDmaDevice);
+                lds_dma16<true>((const u32x4 *)src + i, (u32x4 *)dst + i0);
         }
     };
     // t and s of the MF rows into this wave's LDS region, copied from the
@@ -430,25 +462,36 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     }
     const int64_t gw = bid * 4 + wv, nw = (int64_t)a.nwg * 4;
 
-    DPair<NV> P0, P1;
-    load_pair(P0, 0);
-    load_pair(P1, 1);
-    {   // residual scales and X into LDS
+    {   // residual scales, row scales of the low-rank terms and X into LDS,
+        // issued before the first prefetches so that the wait for them
+        // leaves the prefetches in flight
         const int64_t nvb_wg = (nvb - wg_vb0) < 4 * NV ? (nvb - wg_vb0) : 4 * NV;
-        const int64_t nsr = nvb_wg * G * kVB / 8, nx = MF * d / 8;
+        const int64_t nsr = nvb_wg * G * kVB / 8, nsa = nvb_wg * kVB / 8, nx = MF * d / 8;
         for (int64_t i0 = 0; i0 < nsr; i0 += 256) {
             const int64_t i = i0 + threadIdx.x;
             if (i < nsr)
-                __builtin_amdgcn_global_load_lds((const void *)((const u32x4 *)(a.h.sr + wg_vb0 * G * kVB) + i),
-                                                 (__attribute__((address_space(3))) void *)((u32x4 *)smem + i0 + wv * 64), 16, 0, 0);
+                lds_dma16<false>((const u32x4 *)(a.h.sr + wg_vb0 * G * kVB) + i, (u32x4 *)smem + i0 + wv * 64);
+        }
+        if (threadIdx.x < 64) {
+            for (int64_t i0 = 0; i0 < nsa; i0 += 64)
+                if (i0 + lane < nsa) {
+                    lds_dma16<false>((const u32x4 *)(a.h.sa + wg_vb0 * kVB) + i0 + lane, (u32x4 *)(smem + a.lds_sa) + i0);
+                    lds_dma16<false>((const u32x4 *)(a.h.sc + wg_vb0 * kVB) + i0 + lane,
+                                     (u32x4 *)(smem + a.lds_sa) + 4 * NV * kVB / 8 + i0);
+                }
         }
         for (int64_t i0 = 0; i0 < nx; i0 += 256) {
             const int64_t i = i0 + threadIdx.x;
             if (i < nx)
-                __builtin_amdgcn_global_load_lds((const void *)((const u32x4 *)a.X + i),
-                                                 (__attribute__((address_space(3))) void *)((u32x4 *)(smem + a.lds_x) + i0 + wv * 64), 16, 0, 0);
+                lds_dma16<false>((const u32x4 *)a.X + i, (u32x4 *)(smem + a.lds_x) + i0 + wv * 64);
         }
     }
+    DPair<NV> P0, P1;
+    load_pair(P0, 0);
+    load_pair(P1, 1);
+    // this wave's copies have landed once at most its 4 NV prefetches are
+    // outstanding; after the barrier, every wave's have
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NV));
     __syncthreads();
     if (a.ntwg == 0)
         for (int64_t i = gw; i < ntask; i += nw)
@@ -730,41 +773,45 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     };
 
     // One control path for every shape (separate paths for the cases made
-    // the register allocator spill the prefetch buffers).  The last
+    // the register allocator spill the prefetch buffers).  The second-last
     // iteration before the low-rank pairs reads the count of published
     // columns, issued ahead of the iteration's prefetch so that waiting for
     // it costs nothing (loads complete in order).  The count grows by k + r
     // per call and is never reset, so it equals (k + r)(calls before + 1)
     // exactly when this call has published every column.  t and s are then
-    // copied to LDS (a copy issued inside the loops would cost registers);
-    // if the count fell short, the column flags tell which columns the wave
+    // copied to LDS at the start of the last iteration and waited for at its
+    // end, where only that iteration's prefetches may still be in flight; if
+    // the count fell short, the column flags tell which columns the wave
     // must compute itself.
     int64_t pi = 0;
-    for (; pi + 2 < nrp1; pi += 2)
+    for (; pi + 4 < nrp1; pi += 2)
         res_iter(pi, 2 * pi, true);
     uint32_t seen = 0;
-    if (nrp1 >= 2) {
+    if (nrp1 >= 4) {
         seen = __hip_atomic_load(sync + sync_published(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        res_iter(pi, 2 * pi, true);
+        pi += 2;
+    }
+    const bool ready = nlr > 0 && nrp1 >= 4 &&
+                       __builtin_amdgcn_readfirstlane(seen) ==
+                           (uint32_t)ntask * (__builtin_amdgcn_readfirstlane(epoch) + 1u);
+    if (ready)
+        stage_ts();
+    if (nrp1 >= 2) {
         res_iter(pi, 2 * pi, true);
         pi += 2;
     }
     flush_mx(2 * pi - 1);
     if (nlr > 0) {
-        const bool ready = nrp1 >= 2 && __builtin_amdgcn_readfirstlane(seen) ==
-                                            (uint32_t)ntask * (__builtin_amdgcn_readfirstlane(epoch) + 1u);
         if (ready) {
-            stage_ts();
-            wait_vm_all(); // the copy has landed
+            // the copy has landed once at most the 4 NV prefetches issued
+            // after it are outstanding
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NV));
+            asm volatile("" ::: "memory");
         } else {
             build_ts();
+            wait_vm_all();
         }
-    }
-    // row scales of the low-rank terms, consumed after the low-rank pairs
-    float sa[NV], sc[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        sa[v] = h2f(a.h.sa[vb[v] * kVB + lr]);
-        sc[v] = h2f(a.h.sc[vb[v] * kVB + lr]);
     }
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
@@ -781,16 +828,18 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     for (; pi < nrp1 + nlp; pi += 2)
         lr_iter(pi);
     // tot += sA (A5 t - 144 sum t) + sC (C8 s)
+    const uint16_t *s_sa = (const uint16_t *)(smem + a.lds_sa) + wv * NV * kVB;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
+        const float sa = h2f(s_sa[v * kVB + lr]), sc = h2f(s_sa[4 * NV * kVB + v * kVB + lr]);
         if constexpr (MX) {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
-                acc[v][m] = __builtin_fmaf(sa[v], gam[v][m] + ntm[m], __builtin_fmaf(sc[v], gcm[v][m], acc[v][m]));
+                acc[v][m] = __builtin_fmaf(sa, gam[v][m] + ntm[m], __builtin_fmaf(sc, gcm[v][m], acc[v][m]));
         } else {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
-                tot[v][m] = __builtin_fmaf(sa[v], ga[v][m] + nt[m], __builtin_fmaf(sc[v], gc[v][m], tot[v][m]));
+                tot[v][m] = __builtin_fmaf(sa, ga[v][m] + nt[m], __builtin_fmaf(sc, gc[v][m], tot[v][m]));
         }
     }
     for (; pi + 2 < npairs; pi += 2)
@@ -836,9 +885,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     };
 
     // ---- a3: workgroup maximum per row; then per slot of workgroups (the
-    // workgroups b with b % nslot == s) an atomic max and a count, and the
-    // last workgroup of each slot passes its slot's keys on to the grid's;
-    // the last slot resolves the keys and resets every counter ----
+    // workgroups b with b % nslot == s) an atomic max and a count; the last
+    // workgroup of each slot counts the slot as done, and the last slot
+    // reads every slot's keys, resolves them and resets every counter ----
     if (a.argmax) {
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
@@ -859,36 +908,39 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         return;
     }
     // wave 0.  Device-scope atomics are performed at the device's coherence
-    // point; each is complete before the count that follows it.
+    // point; each is complete before the count that follows it, so a slot's
+    // keys are final once its count is full, and every key is final once
+    // every slot is counted.
     const int nslot = a.nwg < kSyncGroups ? a.nwg : kSyncGroups;
     const int slot = (int)(bid % nslot);
     const uint32_t slot_size = (uint32_t)((a.nwg - 1 - slot) / nslot + 1);
-    uint64_t *const slot_key = a.w.keys + slot * 32, *const top_key = a.w.keys + kSyncGroups * 32;
     if (a.argmax && lane < MF) {
         const uint64_t kk = umax64(umax64(red[0][lane], red[1][lane]), umax64(red[2][lane], red[3][lane]));
-        __hip_atomic_fetch_max(slot_key + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(a.w.keys + slot * 32 + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm_all();
     uint32_t prev = 0;
     if (lane == 0)
         prev = __hip_atomic_fetch_add(sync + sync_slot_done(slot), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
-        if (lane == 0)
-            __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (a.argmax && lane < MF) {
-            const uint64_t kk =
-                __hip_atomic_exchange(slot_key + lane, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_max(top_key + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        wait_vm_all();
         uint32_t prev2 = 0;
-        if (lane == 0)
+        if (lane == 0) {
+            __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
-            if (a.argmax && lane < MF) {
-                const uint64_t kk =
-                    __hip_atomic_exchange(top_key + lane, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+            if (a.argmax) {
+                // lane s * MF + m takes (and clears) key m of slot s
+                const int s = lane / MF, m = lane % MF;
+                uint64_t kk = 0;
+                if (s < nslot)
+                    kk = __hip_atomic_exchange(a.w.keys + s * 32 + m, (uint64_t)0, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int off = MF; off < kSyncGroups * MF; off <<= 1)
+                    kk = umax64(kk, shfl_xor_u64(kk, off));
+                if (lane < MF)
+                    a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
             }
             if (lane == 0) {
                 __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -905,14 +957,15 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 static size_t dal16(size_t x) { return (x + 15) / 16 * 16; }
 
 struct DecodeLds {
-    unsigned x, ts;
+    unsigned sa, x, ts;
     size_t total;
 };
 
 static DecodeLds decode_lds(const Shape &s, int64_t M)
 {
     DecodeLds L;
-    L.x = (unsigned)dal16(size_t(4) * decode_nv((int)M) * s.G() * kVB * 2);
+    L.sa = (unsigned)dal16(size_t(4) * decode_nv((int)M) * s.G() * kVB * 2);
+    L.x = (unsigned)(L.sa + size_t(2) * 4 * decode_nv((int)M) * kVB * 2);
     L.ts = (unsigned)(L.x + dal16(size_t(M) * s.d * 2));
     L.total = L.ts + size_t(4) * 2 * M * (s.kpad() + s.rpad()) * 2;
     return L;
@@ -987,6 +1040,7 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     // free (two workgroups per CU), at least one column per wave
     const int64_t spare = int64_t(2) * h.n_cu - a.nwg;
     a.ntwg = spare > 0 ? (int)std::min<int64_t>(spare, (a.ntask + 3) / 4) : 0;
+    a.lds_sa = L.sa;
     a.lds_x = L.x;
     a.lds_ts = L.ts;
     if (L.total > 64 * 1024) {

@@ -137,12 +137,11 @@ constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path
 //   epoch         calls completed (never reset; tags the column flags)
 //   top_done      slots finished
 //   published     projection columns published (never reset: k + r per call)
-// and the argmax keys: per slot s, keys[s * 32 + m]; the grid's,
-// keys[kSyncGroups * 32 + m], m < kDecodeMaxM.
+// and the argmax keys: per slot s, keys[s * 32 + m], m < kDecodeMaxM.
 constexpr int kSyncGroups = 16;
 constexpr int kSyncStride = 64; // uint32 per 256-byte line
 constexpr size_t kSyncWords = size_t(2 * kSyncGroups + 3) * kSyncStride;
-constexpr size_t kKeyWords = size_t(kSyncGroups + 1) * 32;
+constexpr size_t kKeyWords = size_t(kSyncGroups) * 32;
 __host__ __device__ constexpr size_t sync_slot_done(int s) { return size_t(kSyncGroups + s) * kSyncStride; }
 __host__ __device__ constexpr size_t sync_epoch() { return size_t(2 * kSyncGroups) * kSyncStride; }
 __host__ __device__ constexpr size_t sync_top_done() { return size_t(2 * kSyncGroups + 1) * kSyncStride; }
