@@ -125,8 +125,7 @@ __device__ __forceinline__ void step_fence()
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin4(f32x4 &x) { asm volatile("" : "+v"(x)); }
 
-constexpr uint32_t kBf16Neg136 = 0xC308C308u; // bf16 pair (-136, -136)
-constexpr uint32_t kBf16Neg144 = 0xC310C310u; // bf16 pair (-144, -144)
+constexpr uint32_t kBf16One = 0x3F803F80u; // bf16 pair (1, 1)
 
 struct DecodeArgs {
     DevHead h;
@@ -140,7 +139,7 @@ struct DecodeArgs {
     int ntwg;        // projection-only workgroups, first in the grid (0: the
                      // streaming waves compute the columns themselves)
     int nwg;         // streaming workgroups, after them
-    unsigned lds_sa, lds_x, lds_ts; // byte offsets of the sA/sC, X and t/s regions (sr at 0)
+    unsigned lds_sa, lds_x, lds_ts, lds_xs; // byte offsets of the sA/sC, X, t/s and group-sum regions (sr at 0)
 };
 
 // v-blocks per wave: five at M = 1, four at M = 2 (whose accumulators need
@@ -162,6 +161,8 @@ struct DPair {
 //   sa  [2][4*NV][16]        fp16  sA, then sC, of its rows
 //   x   [MF][d]              bf16  the hidden states
 //   ts  [4 waves] x { t hi [MF][kpad], t lo [MF][kpad], s hi [MF][rpad], s lo [MF][rpad] }  bf16
+//   xs  [4 waves][MF][G]     fp32  -136 (sum of X over group grp), a
+//                                  quarter of it in the VALU variant
 //
 // A wave's chunk stream: the first three quarters of the residual K-chunks,
 // then the low-rank chunks, then the remaining residual K-chunks.  Placing the low-rank chunks
@@ -497,15 +498,34 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         for (int64_t i = gw; i < ntask; i += nw)
             publish((int)i);
 
+    // The offset of the residual codes, -136 sum_{j in grp} X[m,j], for
+    // every group, once per wave: in the VALU variant each of the four lanes
+    // of a row adds a quarter.  A lane sums one group, starting at a piece
+    // that depends on the lane, so that lanes reading groups a multiple of
+    // the LDS banks apart do not all meet in one bank.
+    float *const s_xs = (float *)(smem + a.lds_xs) + wv * MF * G;
+    {
+        const uint32_t one = vgpr_const(kBf16One);
+        const int pg = (int)(a.h.s.g / 8), nG = (int)G;
+        for (int i = lane; i < MF * nG; i += 64) {
+            const uint16_t *xp = s_x + (i / nG) * d + (int64_t)(i % nG) * a.h.s.g;
+            float sum = 0.f;
+            int pp = lane % pg;
+            for (int p = 0; p < pg; ++p) {
+                sum = dot8c(*(const u32x4 *)(xp + 8 * pp), one, sum);
+                pp = pp + 1 == pg ? 0 : pp + 1;
+            }
+            s_xs[i] = (MX ? -136.f : -34.f) * sum;
+        }
+    }
+
     // VALU variant: per-lane partial sums over the lane's columns
-    float tot[NV][MF], g[NV][MF], xn[MF];
+    float tot[NV][MF], g[NV][MF];
 #pragma unroll
-    for (int m = 0; m < MF; ++m) {
-        xn[m] = 0.f;
+    for (int m = 0; m < MF; ++m)
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             tot[v][m] = g[v][m] = 0.f;
-    }
     // matrix-core variant: [16 rows of X (row m in lanes 16(m/4)..) x 16
     // vocabulary rows] tiles; lane l holds rows 4(l/16) + i of column l % 16.
     // Chunk kc accumulates into gq[kc & 1] and is folded one chunk later
@@ -513,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // Only rows m < MF of the tiles are kept in the running totals (lanes
     // 0..15 hold them, MF <= 4).
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 gq[2][NV], nx[2];
+    f32x4 gq[2][NV];
     float acc[NV][MF];
     bool pend = false; // chunk kc - 1 still to fold
 #pragma unroll
@@ -523,16 +543,18 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             acc[v][m] = 0.f;
     const int64_t xrow = lr < MF ? lr : MF - 1; // A-operand rows past M repeat the last row
     const uint32_t kMagic = vgpr_const(kBf16Magic);
-    const uint32_t c136 = vgpr_const(kBf16Neg136), c144 = vgpr_const(kBf16Neg144);
-    const u32x4 c136x4 = {c136, c136, c136, c136}, c144x4 = {c144, c144, c144, c144};
 
     auto fold_mx = [&](int sel, int64_t kc) __attribute__((always_inline)) {
+        float xo[MF];
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+            xo[m] = s_xs[m * G + kc];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const float scl = h2f(s_sr[((wv * NV + v) * G + kc) * kVB + lr]);
 #pragma unroll
             for (int m = 0; m < MF; ++m)
-                acc[v][m] = __builtin_fmaf(scl, gq[sel][v][m] + nx[sel][m], acc[v][m]);
+                acc[v][m] = __builtin_fmaf(scl, gq[sel][v][m] + xo[m], acc[v][m]);
         }
     };
     auto flush_mx = [&](int64_t kc_last) __attribute__((always_inline)) {
@@ -555,13 +577,11 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             for (int s = 0; s < 4; ++s) {
                 const int64_t ks = kc * 4 + s;
                 const u32x4 xa = *(const u32x4 *)(s_x + xrow * d + ks * kKStep + 8 * lq);
-                nx[sel] = mfma_bf16(xa, c136x4, s == 0 ? zero4 : nx[sel]);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     const uint32_t wd = s == 0 ? c.q[v].x : s == 1 ? c.q[v].y : s == 2 ? c.q[v].z : c.q[v].w;
                     gq[sel][v] = mfma_bf16(xa, r4_bf16(wd, kMagic), s == 0 ? zero4 : gq[sel][v]);
                 }
-                pin4(nx[sel]);
 #pragma unroll
                 for (int v = 0; v < NV; ++v)
                     pin4(gq[sel][v]);
@@ -580,7 +600,6 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
                 x[m] = *(const u32x4 *)(s_x + m * d + ks * kKStep + 8 * lq);
-                xn[m] = dot8c(x[m], c136, xn[m]);
             }
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -598,31 +617,26 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     const float scl = h2f(s_sr[((wv * NV + v) * G + grp) * kVB + lr]);
 #pragma unroll
                     for (int m = 0; m < MF; ++m) {
-                        tot[v][m] = __builtin_fmaf(scl, g[v][m] + xn[m], tot[v][m]);
+                        tot[v][m] = __builtin_fmaf(scl, g[v][m] + s_xs[m * G + grp], tot[v][m]);
                         g[v][m] = 0.f;
                     }
                 }
-#pragma unroll
-                for (int m = 0; m < MF; ++m)
-                    xn[m] = 0.f;
             }
             // one K-step at a time: the hidden-state fragments and
             // dequantised codes of later K-steps are not hoisted into
             // registers early, nor this step's arithmetic sunk late
 #pragma unroll
-            for (int m = 0; m < MF; ++m) {
-                pin(xn[m]);
+            for (int m = 0; m < MF; ++m)
 #pragma unroll
                 for (int v = 0; v < NV; ++v)
                     pin(g[v][m]);
-            }
             step_fence();
         }
     };
     // low-rank chunk j: three core K-steps (A5 + 16 against t) or two
     // correction K-steps (C8 against s); K-steps beyond the rank are skipped
-    float ga[NV][MF], gc[NV][MF], nt[MF];
-    f32x4 gam[NV], gcm[NV], ntm;
+    float ga[NV][MF], gc[NV][MF];
+    f32x4 gam[NV], gcm[NV];
     const uint16_t *s_t = s_ts, *s_s = s_ts + 2 * MF * kpad;
     auto lr_chunk = [&](const DChunk<NV> &c, int64_t j) __attribute__((always_inline)) {
         if constexpr (MX) {
@@ -634,14 +648,12 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                         break;
                     const u32x4 th = *(const u32x4 *)(s_t + xrow * kpad + ks * kKStep + 8 * lq);
                     const u32x4 tl = *(const u32x4 *)(s_t + (MF + xrow) * kpad + ks * kKStep + 8 * lq);
-                    ntm = mfma_bf16(tl, c144x4, mfma_bf16(th, c144x4, ntm));
 #pragma unroll
                     for (int v = 0; v < NV; ++v) {
                         const uint32_t wn = q == 0 ? c.q[v].x : q == 1 ? c.q[v].y : c.q[v].z;
                         const u32x4 b = a5_bf16_q(wn, c.q[v].w, q);
                         gam[v] = mfma_bf16(tl, b, mfma_bf16(th, b, gam[v]));
                     }
-                    pin4(ntm);
 #pragma unroll
                     for (int v = 0; v < NV; ++v)
                         pin4(gam[v]);
@@ -682,7 +694,6 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 for (int m = 0; m < MF; ++m) {
                     th[m] = *(const u32x4 *)(s_t + m * kpad + ks * kKStep + 8 * lq);
                     tl[m] = *(const u32x4 *)(s_t + (MF + m) * kpad + ks * kKStep + 8 * lq);
-                    nt[m] = dot8c(tl[m], c144, dot8c(th[m], c144, nt[m]));
                 }
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
@@ -693,12 +704,10 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                         ga[v][m] = dot8(tl[m], b, dot8(th[m], b, ga[v][m]));
                 }
 #pragma unroll
-                for (int m = 0; m < MF; ++m) {
-                    pin(nt[m]);
+                for (int m = 0; m < MF; ++m)
 #pragma unroll
                     for (int v = 0; v < NV; ++v)
                         pin(ga[v][m]);
-                }
                 step_fence();
             }
         } else {
@@ -813,14 +822,26 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             wait_vm_all();
         }
     }
+    // the offset of the core codes, -144 sum_i t[m,i] (hi and lo parts),
+    // once per wave (in the VALU variant a quarter per lane of a row)
+    float nto[MF];
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
-        nt[m] = 0.f;
+        const uint32_t one = vgpr_const(kBf16One);
+        float sum = 0.f;
+        for (int64_t i = lane; i < kpad / 8; i += 64) {
+            sum = dot8c(*(const u32x4 *)(s_t + m * kpad + 8 * i), one, sum);
+            sum = dot8c(*(const u32x4 *)(s_t + (MF + m) * kpad + 8 * i), one, sum);
+        }
+        for (int off = 32; off >= 1; off >>= 1)
+            sum += __shfl_xor(sum, off);
+        nto[m] = (MX ? -144.f : -36.f) * sum;
+    }
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             ga[v][m] = gc[v][m] = 0.f;
-    }
-    ntm = zero4;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         gam[v] = gcm[v] = zero4;
@@ -835,11 +856,11 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         if constexpr (MX) {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
-                acc[v][m] = __builtin_fmaf(sa, gam[v][m] + ntm[m], __builtin_fmaf(sc, gcm[v][m], acc[v][m]));
+                acc[v][m] = __builtin_fmaf(sa, gam[v][m] + nto[m], __builtin_fmaf(sc, gcm[v][m], acc[v][m]));
         } else {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
-                tot[v][m] = __builtin_fmaf(sa, ga[v][m] + nt[m], __builtin_fmaf(sc, gc[v][m], tot[v][m]));
+                tot[v][m] = __builtin_fmaf(sa, ga[v][m] + nto[m], __builtin_fmaf(sc, gc[v][m], tot[v][m]));
         }
     }
     for (; pi + 2 < npairs; pi += 2)
@@ -957,7 +978,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 static size_t dal16(size_t x) { return (x + 15) / 16 * 16; }
 
 struct DecodeLds {
-    unsigned sa, x, ts;
+    unsigned sa, x, ts, xs;
     size_t total;
 };
 
@@ -967,7 +988,8 @@ static DecodeLds decode_lds(const Shape &s, int64_t M)
     L.sa = (unsigned)dal16(size_t(4) * decode_nv((int)M) * s.G() * kVB * 2);
     L.x = (unsigned)(L.sa + size_t(2) * 4 * decode_nv((int)M) * kVB * 2);
     L.ts = (unsigned)(L.x + dal16(size_t(M) * s.d * 2));
-    L.total = L.ts + size_t(4) * 2 * M * (s.kpad() + s.rpad()) * 2;
+    L.xs = (unsigned)dal16(L.ts + size_t(4) * 2 * M * (s.kpad() + s.rpad()) * 2);
+    L.total = L.xs + size_t(4) * M * s.G() * 4;
     return L;
 }
 
@@ -1043,6 +1065,7 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     a.lds_sa = L.sa;
     a.lds_x = L.x;
     a.lds_ts = L.ts;
+    a.lds_xs = L.xs;
     if (L.total > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
         if (e != hipSuccess)
