@@ -36,12 +36,14 @@
 //       columns as offset-binary bytes (c ^ 0x80) in natural order.  The chunk
 //       count n_lr is padded to a multiple of 4; K-steps beyond kst / rst hold
 //       the code of zero and are skipped.
-//  srp  uint16 [nvb][G][16]          sR * 2^e_v in fp16, an exact power-of-two
-//       rescale with e_v per row such that the row's largest scale (over its
-//       sR groups, sA and sC) lies in [1, 2); the large-M kernel multiplies
-//       the codes by these in fp16.
-//  sap, scp uint16 [nvb*16]          sA * 2^e_v and sC * 2^e_v in fp16.
-//  rsc  float  [nvb*16]              2^-e_v per row.
+//  srp  uint16 [nvb][G][16]          sR * 2^(e_r + 14) in fp16, an exact
+//       power-of-two rescale with e_r per row such that the row's largest
+//       residual scale lies in [2^14, 2^15); the large-M kernel turns each
+//       code q into the fp16 value q sR 2^(e_r - 10) with one fused
+//       multiply-add.
+//  sap, scp uint16 [nvb*16]          sA * 2^e_v and sC * 2^e_v in fp16, e_v
+//       per row such that the row's largest of sR, sA, sC lies in [1, 2).
+//  rsc  float  [nvb*16]              2^(10 - e_r) per row.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
 //  d8   int8   [r][d], sd float [r][G]  quantised B_w and its group scales.

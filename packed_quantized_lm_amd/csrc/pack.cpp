@@ -99,12 +99,18 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
             for (int64_t c = 0; live && c < G; ++c)
                 mx = std::max(mx, std::fabs(half_to_float(sR[row * G + c])));
             const int e = (mx > 0.f && std::isfinite(mx)) ? -std::ilogb(mx) : 0;
+            // the residual scales on their own: the row's largest into
+            // [2^14, 2^15)
+            float mr = 0.f;
+            for (int64_t c = 0; live && c < G; ++c)
+                mr = std::max(mr, std::fabs(half_to_float(sR[row * G + c])));
+            const int er = (mr > 0.f && std::isfinite(mr)) ? -std::ilogb(mr) : 0;
             for (int64_t c = 0; c < G; ++c)
                 o.srp[(vb * G + c) * kVB + i] =
-                    live ? float_to_half(std::ldexp(half_to_float(sR[row * G + c]), e)) : 0;
+                    live ? float_to_half(std::ldexp(half_to_float(sR[row * G + c]), er + 14)) : 0;
             o.sap[row] = float_to_half(std::ldexp(sa, e));
             o.scp[row] = float_to_half(std::ldexp(sc, e));
-            o.rsc[row] = std::ldexp(1.0f, -e);
+            o.rsc[row] = std::ldexp(1.0f, 10 - er);
             o.sa[row] = (live && k > 0) ? sA[row] : 0;
             o.sc[row] = (live && r > 0) ? sC[row] : 0;
         }

@@ -144,26 +144,43 @@ __global__ __launch_bounds__(256) void prep_lds_kernel(PrepArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// B-operand dequantisation: integer codes -> exact fp16 integers (exponent
-// splicing: 0x6400 | u = 1024 + u for u < 1024, then one exact subtraction)
-// -> times the row's fp16 scale, rounded once.
+// B-operand dequantisation.
+//
+// Residual: a nibble u = q + 8 masked into bits 0-3 (4-7) of an fp16 half is
+// the subnormal u 2^-24 (u 2^-20).  With S = srp = sR 2^(e_r + 14) (a
+// normal fp16 below 2^15), one fused multiply-add per column pair,
+//   u 2^-24 (S) + (-S 2^-21) = (u - 8) S 2^-24 = q sR 2^(e_r - 10),
+//   u 2^-20 (S 2^-4) + (-S 2^-21) = the same,
+// gives the product rounded once: the product of the two operands is exact
+// inside the fma, and -S 2^-21 = -8 S 2^-24 is an exact normal fp16.  The
+// kernel runs with fp16 denormals kept (the default mode).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t f16x2_code_times(uint32_t spliced, float bias, f16x2 s2)
+struct R4Scale {
+    f16x2 m0, m1, c; // S, S 2^-4, -S 2^-21 in both halves
+};
+
+__device__ __forceinline__ R4Scale r4_scale(uint32_t srp_bits)
 {
-    const f16x2 b = {(_Float16)bias, (_Float16)bias};
-    f16x2 h = __builtin_bit_cast(f16x2, spliced) - b; // exact: the signed code
-    h = h * s2;                                       // rounded once
-    return __builtin_bit_cast(uint32_t, h);
+    R4Scale r;
+    r.m0 = __builtin_bit_cast(f16x2, srp_bits * 0x10001u);
+    r.m1 = r.m0 * f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+    r.c = r.m0 * f16x2{(_Float16)-4.76837158203125e-07f, (_Float16)-4.76837158203125e-07f}; // -2^-21
+    return r;
 }
 
-// residual dword (8 offset-binary nibbles, slot order of layout.hpp)
-__device__ __forceinline__ u32x4 r4_f16(uint32_t w, uint32_t magic, f16x2 s2)
+__device__ __forceinline__ uint32_t f16x2_fma(uint32_t a, f16x2 b, f16x2 c)
 {
-    const uint32_t m = 0x000F000Fu;
-    return u32x4{f16x2_code_times((w & m) | magic, 1032.f, s2),
-                 f16x2_code_times(((w >> 4) & m) | magic, 1032.f, s2),
-                 f16x2_code_times(((w >> 8) & m) | magic, 1032.f, s2),
-                 f16x2_code_times(((w >> 12) & m) | magic, 1032.f, s2)};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, a), b, c));
+}
+
+// residual dword (8 offset-binary nibbles, slot order of layout.hpp): column
+// pairs (0,1), (2,3), (4,5), (6,7) are the nibble pairs at bits (0,16),
+// (4,20), (8,24), (12,28)
+__device__ __forceinline__ u32x4 r4_f16(uint32_t w, const R4Scale &sc)
+{
+    const uint32_t w8 = w >> 8;
+    return u32x4{f16x2_fma(w & 0x000F000Fu, sc.m0, sc.c), f16x2_fma(w & 0x00F000F0u, sc.m1, sc.c),
+                 f16x2_fma(w8 & 0x000F000Fu, sc.m0, sc.c), f16x2_fma(w8 & 0x00F000F0u, sc.m1, sc.c)};
 }
 
 // exact fp16 integers from spliced codes: (1024 + u) - bias
@@ -268,8 +285,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         nz |= h2f(a.h.sc[vb[v] * kVB + lr]) != 0.f ? 1u << (kLVB + v) : 0u;
     }
     // unit divisors: sA (sC) of the lane's row, or 1 where it is zero
-    auto pa = [&](int v) { const float x = h2f(a.h.sa[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
-    auto pc = [&](int v) { const float x = h2f(a.h.sc[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
+    auto pa = [&](int v) __attribute__((always_inline)) { const float x = h2f(a.h.sa[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
+    auto pc = [&](int v) __attribute__((always_inline)) { const float x = h2f(a.h.sc[vb[v] * kVB + lr]); return x != 0.f ? x : 1.f; };
     if (threadIdx.x < kLRows) {
         const int64_t m = mbase + threadIdx.x; // below the prepared row count
         s_fm[threadIdx.x] = a.w.xsc[2 * m + 1];      // 2^f_m
@@ -282,11 +299,14 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     const int fq = (wv * kLS) >> 3, fmb0 = (wv * kLS) & 7;
     const uint32_t *lrw = a.h.lr, *r4w = a.h.r4;
     const int64_t chunk_words = nvb * 256; // uint32 words of one K-chunk of one stream
+    // every copy reads a wave-uniform base plus one of two per-lane byte
+    // offsets (no per-lane 64-bit address stays live across the stages)
+    const uint32_t lane16 = (uint32_t)lane * 16u;
     // residual-scale rows this lane copies: v-block lane / 2 of the workgroup
     const int64_t svb = wg_vb0 + (lane >> 1) < nvb ? wg_vb0 + (lane >> 1) : nvb - 1;
-    const int64_t soff = svb * G * kVB + 8 * (lane & 1); // + grp * 16
+    const uint32_t soffb = (uint32_t)(svb * G * kVB + 8 * (lane & 1)) * 2u; // + grp * 32
 
-    auto stage_fill = [&](int64_t s, uint32_t *buf) {
+    auto stage_fill = [&](int64_t s, uint32_t *buf) __attribute__((always_inline)) {
         const int64_t hh = fq >> 1, half = fq & 1;
         const uint16_t *base; // operand block of m-block 0 of the tile
         int64_t mbstride;     // halfs between consecutive m-blocks
@@ -326,21 +346,22 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         }
 #pragma unroll
         for (int i = 0; i < kLS; ++i)
-            lds_dma16(base + (fmb0 + i) * mbstride + lane * 8, buf + (wv * kLS + i) * 256);
+            lds_dma16((const char *)(base + (fmb0 + i) * mbstride) + lane16, buf + (wv * kLS + i) * 256);
         if (s < p2) { // one whole chunk per v-block: [lane][4 words], 16-byte copies
 #pragma unroll
             for (int v = 0; v < kLVB; ++v)
-                lds_dma16(cp[0] + (vb[v] * 64 + lane) * 4, buf + kLCodeOff + (wv * kLVB + v) * 256);
+                lds_dma16((const char *)(cp[0] + vb[v] * 256) + lane16, buf + kLCodeOff + (wv * kLVB + v) * 256);
         } else { // words from up to two chunks: [4 words][lane], 4-byte copies
 #pragma unroll
             for (int v = 0; v < kLVB; ++v)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    lds_dma4(cp[q] + (vb[v] * 64 + lane) * 4 + cw[q], buf + kLCodeOff + (wv * kLVB + v) * 256 + q * 64);
+                    lds_dma4((const char *)(cp[q] + vb[v] * 256 + cw[q]) + lane16,
+                             buf + kLCodeOff + (wv * kLVB + v) * 256 + q * 64);
         }
         if (s < p1 && (GS == 4 ? wv == 0 : wv < 4)) { // kLW >= 4
             const int64_t grp = GS == 4 ? kc : (kc * 4 + wv) / gsteps;
-            lds_dma16(a.h.srp + (soff + grp * kVB), buf + kLScOff + (GS == 4 ? 0 : wv) * (kLVR * 8));
+            lds_dma16((const char *)(a.h.srp + grp * kVB) + soffb, buf + kLScOff + (GS == 4 ? 0 : wv) * (kLVR * 8));
         }
     };
 
@@ -355,13 +376,13 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     const uint32_t magic = vgpr_const(kF16Magic);
     // code words: residual and correction stages hold [lane][4 words] per
     // v-block (read whole), core stages [4 words][lane]
-    auto chunk = [&](const uint32_t *buf, int v) { return *(const u32x4 *)(buf + kLCodeOff + (wv * kLVB + v) * 256 + lane * 4); };
-    auto code = [&](const uint32_t *buf, int v, int q) { return buf[kLCodeOff + (wv * kLVB + v) * 256 + q * 64 + lane]; };
+    auto chunk = [&](const uint32_t *buf, int v) __attribute__((always_inline)) { return *(const u32x4 *)(buf + kLCodeOff + (wv * kLVB + v) * 256 + lane * 4); };
+    auto code = [&](const uint32_t *buf, int v, int q) __attribute__((always_inline)) { return buf[kLCodeOff + (wv * kLVB + v) * 256 + q * 64 + lane]; };
 
     // the three stage kinds; no branch surrounds an MFMA (the accumulator
     // tile would be copied at every join): slots past the end of a phase, and
     // pad stages, have their B operands masked to zero
-    auto mfma_slot = [&](const uint32_t *buf, int q, const u32x4(&bq)[kLVB]) {
+    auto mfma_slot = [&](const uint32_t *buf, int q, const u32x4(&bq)[kLVB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mb = 0; mb < kLMB; ++mb) {
             const u32x4 ax = *(const u32x4 *)(buf + (q * 8 + mb) * 256 + lane * 4);
@@ -370,26 +391,33 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
                 T[mb][v] = mfma_f16(ax, bq[v], T[mb][v]);
         }
     };
-    auto compute_r4 = [&](int64_t s, const uint32_t *buf) {
-        const uint32_t live = s < nkc ? 0xFFFFFFFFu : 0u;
+    auto compute_r4 = [&](int64_t s, const uint32_t *buf) __attribute__((always_inline)) {
+        // pad stages: zero scales make every B operand zero
+        const uint32_t live = s < nkc ? 0xFFFFu : 0u;
         const uint16_t *scb = (const uint16_t *)(buf + kLScOff);
         u32x4 c[kLVB];
 #pragma unroll
         for (int v = 0; v < kLVB; ++v)
             c[v] = chunk(buf, v);
+        R4Scale sc[kLVB];
+        if constexpr (GS == 4)
+#pragma unroll
+            for (int v = 0; v < kLVB; ++v)
+                sc[v] = r4_scale((uint32_t)scb[(wv * kLVB + v) * kVB + lr] & live);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             u32x4 bq[kLVB];
 #pragma unroll
             for (int v = 0; v < kLVB; ++v) {
-                const uint32_t sc = (uint32_t)scb[((GS == 4 ? 0 : q) * kLVR + wv * kLVB + v) * kVB + lr] * 0x10001u;
+                if constexpr (GS != 4)
+                    sc[v] = r4_scale((uint32_t)scb[(q * kLVR + wv * kLVB + v) * kVB + lr] & live);
                 const uint32_t wd = q == 0 ? c[v].x : q == 1 ? c[v].y : q == 2 ? c[v].z : c[v].w;
-                bq[v] = and4(r4_f16(wd, magic, __builtin_bit_cast(f16x2, sc)), live);
+                bq[v] = r4_f16(wd, sc[v]);
             }
             mfma_slot(buf, q, bq);
         }
     };
-    auto compute_c8 = [&](int64_t s, const uint32_t *buf) {
+    auto compute_c8 = [&](int64_t s, const uint32_t *buf) __attribute__((always_inline)) {
         const int64_t j = s - p1;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -405,7 +433,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
             mfma_slot(buf, 2 * hh + 1, bq); // lo part of s
         }
     };
-    auto compute_a5 = [&](int64_t s, const uint32_t *buf) {
+    auto compute_a5 = [&](int64_t s, const uint32_t *buf) __attribute__((always_inline)) {
         const int64_t j = s - p2;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -439,7 +467,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         __syncthreads();                                                           \
     }
 
-    // phase 1: residual, in units of 2^-(e_v + f_m)
+    // phase 1: residual, in units of sR 2^(e_r - 10) 2^-f_m
     ARCHEAD_LDS_PHASE(0, p1, compute_r4)
     // to units of sC 2^-f_m
 #pragma unroll
