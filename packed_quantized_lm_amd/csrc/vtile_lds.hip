@@ -27,9 +27,14 @@
 // and the epilogue multiplies by sA[v] 2^-f_m.  Rows whose sC (sA) is zero
 // have their C8 (A5) codes masked and keep a unit divisor.
 //
-// Tiles are assigned so that the workgroups one XCD runs share v-ranges: the
-// 16 m-tiles of a v-range run on the same XCD at about the same time, so its
-// codes come from HBM once and then from that XCD's L2.
+// Tiles are assigned to the XCDs (workgroup b runs on XCD b mod 8) so that
+// operands are shared in an XCD's L2.  When the m-tile count is a multiple
+// of 8, XCD x owns m-tiles x, x + 8, ... and all XCDs sweep the v-ranges in
+// step: the A operands of an XCD's m-tiles (2.4 MB at M = 2048) stay in its
+// L2, and each v-range's codes come from HBM about once and are then shared
+// through the memory-side cache.  Otherwise an XCD runs all m-tiles of a
+// v-range at about the same time, so that its codes come from HBM once and
+// then from that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -226,6 +231,7 @@ struct LdsArgs {
     int64_t nvb, nkc, G, na, nc, kst, rst;
     int64_t nsr, nsc, nsa; // residual / correction / core stages, each padded to even
     int64_t n_vr, n_mt, n_tiles, per_xcd;
+    int mt_major; // XCD x owns m-tiles x, x + 8, ... (n_mt % 8 == 0)
 };
 
 // direct copies into LDS: lane l's piece lands at dst + l pieces
@@ -261,10 +267,18 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     // lives in scalar registers
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t bid = blockIdx.x;
-    const int64_t L = (bid & 7) * a.per_xcd + (bid >> 3);
-    if (L >= a.n_tiles)
-        return; // the whole workgroup
-    const int64_t vr = L / a.n_mt, mt = L % a.n_mt;
+    int64_t vr, mt;
+    if (a.mt_major) {
+        const int64_t x = bid & 7, j = bid >> 3, mpx = a.n_mt >> 3; // j-th tile of XCD x
+        mt = x + 8 * (j % mpx);
+        vr = j / mpx;
+    } else {
+        const int64_t L = (bid & 7) * a.per_xcd + (bid >> 3);
+        if (L >= a.n_tiles)
+            return; // the whole workgroup
+        vr = L / a.n_mt;
+        mt = L % a.n_mt;
+    }
     const int64_t M = a.w.M, d = a.h.s.d, V = a.h.s.V;
     const int64_t nvb = a.nvb, G = a.G, nkc = a.nkc, kst = a.kst, rst = a.rst;
     // stage ranges: residual [0, p1), correction [p1, p2), core [p2, nst)
@@ -598,6 +612,7 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.n_vr = a.w.n_part;
     a.n_mt = (w.M + kLRows - 1) / kLRows;
     a.n_tiles = a.n_vr * a.n_mt;
+    a.mt_major = a.n_mt % 8 == 0;
     const int64_t grid = (a.n_tiles + 7) / 8 * 8;
     a.per_xcd = grid / 8;
     if (a.gsteps == 4)
