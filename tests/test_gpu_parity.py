@@ -111,6 +111,31 @@ def test_multi_tile_shapes(shape, path):
     h.close()
 
 
+# --- residual group scales spread over a wide range -----------------------------------
+
+@pytest.mark.parametrize("path", PATHS)
+def test_wide_residual_scale_spread(path):
+    """Residual group scales of each row spread over 2^-12 .. 1 times 1e-2,
+    with some groups zero.  On the large-M path the residual operand
+    q sR 2^(e_r - 10) then runs from normal fp16 deep into the subnormal
+    range, where its absolute error stays at most 2^-25; the logits must
+    still meet the tolerance (ARCHead paper, eq 7 with the residual of eq 3)."""
+    V, d, k, r, g, M = 700, 512, 32, 8, 32, 150
+    say(f"wide residual scale spread path={path}")
+    f = random_small_head(V, d, k, r, g, M, seed=4242, n_outliers=2, outlier_factor=20.0)
+    rng = np.random.default_rng(4243)
+    G = d // g
+    sr = 1e-2 * np.exp2(-rng.uniform(0.0, 12.0, size=(V, G)))
+    sr[rng.random((V, G)) < 0.05] = 0.0
+    f["sR"] = to_f16_bits(sr)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    y, a = gpu_forward(h, f["X"], path=path)
+    assert_logits_close(y, ref, what=f"wide sR spread, {path}")
+    assert_argmax_ok(a, y, ref, what=f"wide sR spread, {path}")
+    h.close()
+
+
 # --- integer fields read back exactly through the kernels ------------------------------
 
 def _onehot(d, cols):
