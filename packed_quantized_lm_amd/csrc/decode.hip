@@ -802,8 +802,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         pi += 2;
     }
     const bool ready = nlr > 0 && nrp1 >= 4 &&
-                       __builtin_amdgcn_readfirstlane(seen) ==
-                           (uint32_t)ntask * (__builtin_amdgcn_readfirstlane(epoch) + 1u);
+                       (uint32_t)__builtin_amdgcn_readfirstlane(seen) ==
+                           (uint32_t)ntask * ((uint32_t)__builtin_amdgcn_readfirstlane(epoch) + 1u);
     if (ready)
         stage_ts();
     if (nrp1 >= 2) {
@@ -943,13 +943,13 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     uint32_t prev = 0;
     if (lane == 0)
         prev = __hip_atomic_fetch_add(sync + sync_slot_done(slot), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
+    if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
         uint32_t prev2 = 0;
         if (lane == 0) {
             __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
             if (a.argmax) {
                 // lane s * MF + m takes (and clears) key m of slot s
                 const int s = lane / MF, m = lane % MF;
