@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, part, sync, keys, colflag, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, sync, keys, colflag, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -104,6 +104,8 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(2) * Mq * s.rpad() * 2);
     L.xsc = off;
     off = align_up(off + size_t(Mq) * 2 * 4);
+    L.lfill = off;
+    off = align_up(off + size_t(lds_stages(s)) * 16 * 4);
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
     L.sync = off;
@@ -156,6 +158,7 @@ Work make_work(archead_t h, int64_t M)
     w.tsw = (uint16_t *)(b + L.tsw);
     w.ssw = (uint16_t *)(b + L.ssw);
     w.xsc = (float *)(b + L.xsc);
+    w.lfill = (int32_t *)(b + L.lfill);
     w.Mq = round_m128(std::max<int64_t>(h->ws_M, 1));
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;

@@ -37,6 +37,8 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
                             hipStream_t st);
 int64_t lds_n_part(const DevHead &h, int64_t M);
 int64_t lds_max_n_part(const Shape &s);
+// stages of the a2-L kernel (rows of its stage-fill table in the workspace)
+int64_t lds_stages(const Shape &s);
 
 // smallest M for which the automatic choice takes a2-L
 constexpr int64_t kLdsMinM = 128;

@@ -118,6 +118,7 @@ struct Work {
     uint16_t *tsw;     // [Mq/16][kst][2][64][8]  fp16 hi/lo of t 2^f_m, same blocks
     uint16_t *ssw;     // [Mq/16][rst][2][64][8]  fp16 hi/lo of s 2^f_m
     float *xsc;        // [Mq][2]  (2^-f_m, 2^f_m)
+    int32_t *lfill;    // [stages][16]  what each stage of the large-M kernel copies
     int64_t Mq;
     uint64_t *part;    // [M][n_part] argmax partial keys
     int64_t n_part;

@@ -61,12 +61,68 @@ constexpr int kLStageWords = kLScOff + 4 * kLVR * 8; // residual scales [4 K-ste
 // that each block is one contiguous 1 KiB copy.  Rows M .. (tile end) are
 // zeros.
 // ---------------------------------------------------------------------------
+// Stages of the tile kernel, in order: nsr residual stages (one K-chunk
+// each), nsc correction stages, nsa core stages; each count padded to even.
+struct LdsStages {
+    int nst, p1, p2; // stage count; the correction and core phases start at p1, p2
+    int nkc, nc, na, kst, rst, gsteps, nks;
+};
+
+static LdsStages lds_stage_info(const Shape &s)
+{
+    LdsStages t;
+    t.nkc = (int)s.nkc();
+    t.nc = (int)s.lr_nc();
+    t.na = (int)s.lr_na();
+    t.kst = (int)s.kst();
+    t.rst = (int)s.rst();
+    t.gsteps = (int)(s.g / kKStep);
+    t.nks = (int)(s.d / kKStep);
+    const int nsr = (t.nkc + 1) / 2 * 2, nsc = (t.nc + 1) / 2 * 2, nsa = ((t.kst + 1) / 2 + 1) / 2 * 2;
+    t.p1 = nsr;
+    t.p2 = nsr + nsc;
+    t.nst = nsr + nsc + nsa;
+    return t;
+}
+
+// Row s of the stage-fill table: what stage s copies, as small integers.
+//   [0] A operand array (0: X, 1: s, 2: t)   [1] its KiB per 16-row m-block
+//   [2 + fq] KiB offset of the A blocks of slot fq at m-block 0
+//   [6] code stream (0: residual, 1: low-rank)   [7], [8] chunks of words 0-1, 2-3
+//   [9] words taken from those chunks, a byte each   [10 + w] residual scale group of wave w
+// The tile adds its own m-block and v-block offsets.
+__device__ void lds_fill_entry(int s, const LdsStages &t, int32_t *e)
+{
+    const bool isr = s < t.p1, isc = !isr && s < t.p2;
+    const int kc = s < t.nkc ? s : t.nkc - 1;
+    const int j1 = s - t.p1 > 0 ? s - t.p1 : 0, j2 = s - t.p2 > 0 ? s - t.p2 : 0;
+    const int rl = t.rst > 0 ? t.rst - 1 : 0, kl = t.kst > 0 ? t.kst - 1 : 0;
+    e[0] = isr ? 0 : isc ? 1 : 2;
+    e[1] = isr ? t.nks : isc ? 2 * t.rst : 2 * t.kst;
+    for (int fq = 0; fq < 4; ++fq) {
+        const int hh = fq >> 1, half = fq & 1;
+        const int ksc = 2 * j1 + hh < rl ? 2 * j1 + hh : rl, ksa = 2 * j2 + hh < kl ? 2 * j2 + hh : kl;
+        e[2 + fq] = isr ? 4 * kc + fq : isc ? 2 * ksc + half : 2 * ksa + half;
+    }
+    const int k0 = 2 * j2 < kl ? 2 * j2 : kl, k1 = 2 * j2 + 1 < kl ? 2 * j2 + 1 : kl;
+    const int jc = j1 < t.nc - 1 ? j1 : (t.nc > 0 ? t.nc - 1 : 0);
+    e[6] = isr ? 0 : 1;
+    e[7] = isr ? kc : isc ? t.na + jc : k0 / 3;
+    e[8] = isr ? kc : isc ? t.na + jc : k1 / 3;
+    e[9] = isr || isc ? (0 | 1 << 8 | 2 << 16 | 3 << 24) : ((k0 % 3) | 3 << 8 | (k1 % 3) << 16 | 3 << 24);
+    for (int w = 0; w < 4; ++w)
+        e[10 + w] = t.gsteps == 4 ? kc : (kc * 4 + w) / t.gsteps;
+    e[14] = e[15] = 0;
+}
+
 struct PrepArgs {
     const uint16_t *X;
     const float *tf32, *sf32;
     int64_t M, d, k, r, kst, rst, kpad, rpad;
     uint16_t *xsw, *tsw, *ssw;
     float *xsc;
+    LdsStages st;
+    int32_t *lfill;
 };
 
 __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
@@ -74,6 +130,9 @@ __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cas
 __global__ __launch_bounds__(256) void prep_lds_kernel(PrepArgs a)
 {
     __shared__ float red[4];
+    if (blockIdx.x == 0)
+        for (int s = threadIdx.x; s < a.st.nst; s += blockDim.x)
+            lds_fill_entry(s, a.st, a.lfill + s * 16);
     const int64_t m = blockIdx.x;
     const bool live = m < a.M;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -311,8 +370,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     // Operand block b = kLS wv + i holds slot q = b / 8, m-block b % 8; so
     // this wave copies slot fq, m-blocks fmb0 .. fmb0 + kLS - 1.
     const int fq = (wv * kLS) >> 3, fmb0 = (wv * kLS) & 7;
-    const uint32_t *lrw = a.h.lr, *r4w = a.h.r4;
-    const int64_t chunk_words = nvb * 256; // uint32 words of one K-chunk of one stream
+    const char *const lrb = (const char *)a.h.lr, *const r4b = (const char *)a.h.r4;
+    const int64_t chunk_bytes = nvb * 1024; // one K-chunk of one stream
     // every copy reads a wave-uniform base plus one of two per-lane byte
     // offsets (no per-lane 64-bit address stays live across the stages)
     const uint32_t lane16 = (uint32_t)lane * 16u;
@@ -320,63 +379,38 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     const int64_t svb = wg_vb0 + (lane >> 1) < nvb ? wg_vb0 + (lane >> 1) : nvb - 1;
     const uint32_t soffb = (uint32_t)(svb * G * kVB + 8 * (lane & 1)) * 2u; // + grp * 32
 
+    // Stage s's copies, from row s of the stage-fill table (written by the
+    // operand preparation; read through scalar loads): a few adds per copy
+    // instead of recomputing the stage's indices in every wave.
+    const char *const abases[3] = {(const char *)a.w.xsw, (const char *)a.w.ssw, (const char *)a.w.tsw};
     auto stage_fill = [&](int64_t s, uint32_t *buf) __attribute__((always_inline)) {
-        const int64_t hh = fq >> 1, half = fq & 1;
-        const uint16_t *base; // operand block of m-block 0 of the tile
-        int64_t mbstride;     // halfs between consecutive m-blocks
-        const uint32_t *cp[4];
-        int cw[4];
-        int64_t kc = 0;
-        if (s < p1) {
-            kc = s < nkc ? s : nkc - 1;
-            base = a.w.xsw + (mb16_0 * nks + kc * 4 + fq) * 512;
-            mbstride = nks * 512;
-            for (int q = 0; q < 4; ++q) {
-                cp[q] = r4w + kc * chunk_words;
-                cw[q] = q;
-            }
-        } else if (s < p2) {
-            const int64_t j = s - p1;
-            const int64_t ks0 = 2 * j + hh, ks = ks0 < rst ? ks0 : rst - 1;
-            base = a.w.ssw + ((mb16_0 * rst + ks) * 2 + half) * 512;
-            mbstride = rst * 2 * 512;
-            const uint32_t *c = lrw + (a.na + (j < a.nc ? j : a.nc - 1)) * chunk_words;
-            for (int q = 0; q < 4; ++q) {
-                cp[q] = c;
-                cw[q] = q;
-            }
-        } else {
-            const int64_t j = s - p2;
-            const int64_t ks0 = 2 * j + hh, ks = ks0 < kst ? ks0 : kst - 1;
-            base = a.w.tsw + ((mb16_0 * kst + ks) * 2 + half) * 512;
-            mbstride = kst * 2 * 512;
-            const int64_t k0 = 2 * j < kst ? 2 * j : kst - 1, k1 = 2 * j + 1 < kst ? 2 * j + 1 : kst - 1;
-            cp[0] = cp[1] = lrw + (k0 / 3) * chunk_words;
-            cp[2] = cp[3] = lrw + (k1 / 3) * chunk_words;
-            cw[0] = (int)(k0 % 3);
-            cw[1] = 3;
-            cw[2] = (int)(k1 % 3);
-            cw[3] = 3;
-        }
+        typedef __attribute__((address_space(4))) const int32_t cint32;
+        const cint32 *e = (cint32 *)a.w.lfill + s * 16;
+        const int arr = e[0];
+        const int64_t mstride = (int64_t)e[1] * 1024;
+        const char *abase = (arr == 0 ? abases[0] : arr == 1 ? abases[1] : abases[2]) + mb16_0 * mstride +
+                            (int64_t)e[2 + fq] * 1024;
+        const char *cs = e[6] ? lrb : r4b;
+        const char *c0 = cs + e[7] * chunk_bytes, *c1 = cs + e[8] * chunk_bytes;
+        const uint32_t wsel = (uint32_t)e[9];
 #pragma unroll
         for (int i = 0; i < kLS; ++i)
-            lds_dma16((const char *)(base + (fmb0 + i) * mbstride) + lane16, buf + (wv * kLS + i) * 256);
+            lds_dma16(abase + (fmb0 + i) * mstride + lane16, buf + (wv * kLS + i) * 256);
         if (s < p2) { // one whole chunk per v-block: [lane][4 words], 16-byte copies
 #pragma unroll
             for (int v = 0; v < kLVB; ++v)
-                lds_dma16((const char *)(cp[0] + vb[v] * 256) + lane16, buf + kLCodeOff + (wv * kLVB + v) * 256);
+                lds_dma16(c0 + vb[v] * 1024 + lane16, buf + kLCodeOff + (wv * kLVB + v) * 256);
         } else { // words from up to two chunks: [4 words][lane], 4-byte copies
 #pragma unroll
             for (int v = 0; v < kLVB; ++v)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    lds_dma4((const char *)(cp[q] + vb[v] * 256 + cw[q]) + lane16,
+                    lds_dma4((q < 2 ? c0 : c1) + vb[v] * 1024 + ((wsel >> (8 * q)) & 0xFF) * 4 + lane16,
                              buf + kLCodeOff + (wv * kLVB + v) * 256 + q * 64);
         }
-        if (s < p1 && (GS == 4 ? wv == 0 : wv < 4)) { // kLW >= 4
-            const int64_t grp = GS == 4 ? kc : (kc * 4 + wv) / gsteps;
-            lds_dma16((const char *)(a.h.srp + grp * kVB) + soffb, buf + kLScOff + (GS == 4 ? 0 : wv) * (kLVR * 8));
-        }
+        if (s < p1 && (GS == 4 ? wv == 0 : wv < 4)) // kLW >= 4
+            lds_dma16((const char *)a.h.srp + (int64_t)e[10 + wv] * (kVB * 2) + soffb,
+                      buf + kLScOff + (GS == 4 ? 0 : wv) * (kLVR * 8));
     };
 
     // ---- compute -----------------------------------------------------------
@@ -556,6 +590,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 // ---------------------------------------------------------------------------
 int64_t lds_max_n_part(const Shape &s) { return (s.nvb() + kLVR - 1) / kLVR; }
 
+int64_t lds_stages(const Shape &s) { return lds_stage_info(s).nst; }
+
 int64_t lds_n_part(const DevHead &h, int64_t M)
 {
     (void)M;
@@ -580,6 +616,8 @@ hipError_t launch_prep_lds(const DevHead &h, const Work &w, const uint16_t *X, h
     a.tsw = w.tsw;
     a.ssw = w.ssw;
     a.xsc = w.xsc;
+    a.st = lds_stage_info(h.s);
+    a.lfill = w.lfill;
     const int64_t rows = (w.M + kLRows - 1) / kLRows * kLRows; // the tiles' rows, <= Mq
     if (rows > w.Mq)
         return hipErrorInvalidValue;
@@ -606,9 +644,10 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.nc = h.s.lr_nc();
     a.kst = h.s.kst();
     a.rst = h.s.rst();
-    a.nsr = (a.nkc + 1) / 2 * 2;                 // one K-chunk per stage
-    a.nsc = (a.nc + 1) / 2 * 2;                  // two correction K-steps per stage
-    a.nsa = ((a.kst + 1) / 2 + 1) / 2 * 2;      // two core K-steps per stage
+    const LdsStages t = lds_stage_info(h.s);
+    a.nsr = t.p1;                  // one K-chunk per stage
+    a.nsc = t.p2 - t.p1;           // two correction K-steps per stage
+    a.nsa = t.nst - t.p2;          // two core K-steps per stage
     a.n_vr = a.w.n_part;
     a.n_mt = (w.M + kLRows - 1) / kLRows;
     a.n_tiles = a.n_vr * a.n_mt;
