@@ -36,6 +36,9 @@ struct StreamArgs {
     int64_t nvb, nkc, G, na, nlr;
     int gsteps;
     int64_t tl_rows; // most rows of t and s an m-tile stages in LDS per hi/lo half
+    int n_mt;        // m-tiles; with a 1-D grid, workgroup b takes v-range b / n_mt and
+                     // m-tile b % n_mt, so the m-tiles of a v-range run side by side
+                     // (their second read of the codes is served by the memory-side cache)
     unsigned lds_xs, lds_x, lds_t, lds_s; // byte offsets of the LDS regions (sr at 0)
 };
 
@@ -74,10 +77,11 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
     const int wv = threadIdx.x >> 6;
     const int64_t nvb = a.nvb, nkc = a.nkc, G = a.G, na = a.na, nlr = a.nlr;
     const int64_t kst = a.h.s.kst(), rst = a.h.s.rst(), kpad = a.h.s.kpad(), rpad = a.h.s.rpad();
-    const int64_t wg_vb0 = (int64_t)blockIdx.x * 4 * NV;
+    const int64_t vrange = (int64_t)blockIdx.x / a.n_mt, mtile = (int64_t)blockIdx.x % a.n_mt;
+    const int64_t wg_vb0 = vrange * 4 * NV;
     const int64_t vb0 = wg_vb0 + wv * NV;
     const int64_t M = a.w.M, Mp = a.w.Mp, d = a.h.s.d, V = a.h.s.V;
-    const int64_t mbase = (int64_t)blockIdx.y * (MT * 16);
+    const int64_t mbase = mtile * (MT * 16);
     const int64_t rows_live = (M - mbase) < MT * 16 ? (M - mbase) : MT * 16;
     const int gsteps = GS ? GS : a.gsteps;
 
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
         const uint64_t k = umax64(umax64(red[0][threadIdx.x], red[1][threadIdx.x]),
                                   umax64(red[2][threadIdx.x], red[3][threadIdx.x]));
         if (m < M)
-            a.w.part[m * a.w.n_part + blockIdx.x] = k;
+            a.w.part[m * a.w.n_part + vrange] = k;
     }
 }
 
@@ -468,6 +472,8 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
 // launchers
 // ---------------------------------------------------------------------------
 constexpr int kNV = 4;   // v-blocks per wave
+constexpr int kNV2 = 5;  // v-blocks per wave with two m-tiles (one workgroup per CU): 475
+                         // workgroups at V = 151936 make two full rounds of the CUs
 constexpr int kNVW = 5;  // v-blocks per wave, wide pipeline (two waves per SIMD)
 constexpr int64_t kXLdsMaxBytes = 48 * 1024;  // X staged in LDS when M*d*2 fits
 constexpr int64_t kTLdsMaxBytes = 64 * 1024;  // t and s staged in LDS when they fit
@@ -488,7 +494,7 @@ static SkinnyPlan skinny_plan(const DevHead &h, int64_t M)
     const int64_t wide_waves = (h.s.nvb() + kNVW - 1) / kNVW;
     p.wide = p.xl && h.s.g == 4 * kKStep && h.s.nkc() % 4 == 0 && h.s.n_lr() % 4 == 0 &&
              wide_waves <= int64_t(h.n_cu) * 4 * 2;
-    p.nv = p.wide ? kNVW : kNV;
+    p.nv = p.wide ? kNVW : (p.MT == 2 ? kNV2 : kNV);
     return p;
 }
 
@@ -521,9 +527,10 @@ static hipError_t launch(K kern, dim3 grid, size_t lds, hipStream_t st, const A 
 template <int MT, bool XL, bool TL>
 static hipError_t launch_gs(const StreamArgs &a, dim3 grid, size_t lds, hipStream_t st)
 {
+    constexpr int nv = MT == 2 ? kNV2 : kNV;
     switch (a.gsteps) {
-    case 4: return launch(vtile_stream_kernel<kNV, MT, 4, XL, TL, false>, grid, lds, st, a);
-    default: return launch(vtile_stream_kernel<kNV, MT, 0, XL, TL, false>, grid, lds, st, a);
+    case 4: return launch(vtile_stream_kernel<nv, MT, 4, XL, TL, false>, grid, lds, st, a);
+    default: return launch(vtile_stream_kernel<nv, MT, 0, XL, TL, false>, grid, lds, st, a);
     }
 }
 
@@ -559,7 +566,8 @@ hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *
     a.lds_t = (unsigned)(a.lds_x + (XL ? al16(size_t(w.M) * h.s.d * 2) : 0));
     a.lds_s = (unsigned)(a.lds_t + (TL ? t_bytes : 0));
     const size_t lds = a.lds_s + (TL ? s_bytes : 0);
-    const dim3 grid((unsigned)a.w.n_part, gy);
+    a.n_mt = (int)gy;
+    const dim3 grid((unsigned)(a.w.n_part * gy));
     if (p.wide)
         return TL ? launch(vtile_stream_kernel<kNVW, 1, 4, true, true, true>, grid, lds, st, a)
                   : launch(vtile_stream_kernel<kNVW, 1, 4, true, false, true>, grid, lds, st, a);
