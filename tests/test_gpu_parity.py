@@ -136,6 +136,47 @@ def test_wide_residual_scale_spread(path):
     h.close()
 
 
+# --- degenerate rows, a zero hidden state and extreme codes -----------------------------
+
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 2), ("skinny", 1), ("skinny", 20), ("skinny", 40),
+                                    ("lds", 130)])
+def test_zero_scales_zero_state_and_extreme_codes(path, M):
+    """Rows whose sA or sC is zero (the large-M path masks their codes and
+    keeps a unit divisor), rows with every scale zero (logits exactly zero,
+    a block of equal maxima for the lowest-index rule), rows at the extreme
+    codes (A5 = -16, R4 = -8, C8 = -128), and a hidden state of zeros (its
+    logits are exactly zero): ARCHead paper, eq 7 with eq 3."""
+    V, d, k, r, g = 1000, 512, 40, 12, 128
+    say(f"degenerate rows path={path} M={M}")
+    f = random_small_head(V, d, k, r, g, M, seed=515 + M, n_outliers=2, outlier_factor=20.0)
+    sa = f["sA"].copy()
+    sc = f["sC"].copy()
+    sr = f["sR"].copy()
+    sa[::7] = 0
+    sc[::5] = 0
+    sa[100:116] = 0
+    sc[100:116] = 0
+    sr[100:116] = 0
+    f["sA"], f["sC"], f["sR"] = sa, sc, sr
+    f["A5"][200:216] = -16
+    f["R4"][200:216] = 0x88
+    f["C8"][200:216] = -128
+    if M > 1: # (at M = 1 the one hidden state stays random)
+        X = f["X"].copy()
+        X[0] = 0
+        f["X"] = X
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    y, a = gpu_forward(h, f["X"], path=path)
+    if M > 1:
+        assert np.all(y[0] == 0.0), "a zero hidden state gives exactly zero logits"
+        assert a[0] == 0, "all-equal logits resolve to the lowest index"
+    assert np.all(y[:, 100:116] == 0.0), "rows with every scale zero give exactly zero logits"
+    assert_logits_close(y, ref, what=f"degenerate rows, {path}, M={M}")
+    assert_argmax_ok(a, y, ref, what=f"degenerate rows, {path}, M={M}")
+    h.close()
+
+
 # --- integer fields read back exactly through the kernels ------------------------------
 
 def _onehot(d, cols):
