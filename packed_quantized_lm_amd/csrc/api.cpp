@@ -236,7 +236,6 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     };
     const size_t o_r4 = place(s.n_r4() * 4), o_sr = place(s.n_sr() * 2);
     const size_t o_srp = place(s.n_sr() * 2), o_rsc = place(s.n_rows() * 4);
-    const size_t o_sap = place(s.n_rows() * 2), o_scp = place(s.n_rows() * 2);
     const size_t o_lr = place(s.n_lr_words() * 4);
     const size_t o_sa = place(s.n_rows() * 2);
     const size_t o_sc = place(s.n_rows() * 2), o_b8 = place(size_t(k) * d);
@@ -252,7 +251,7 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     }
     char *hb = host.data();
     HostDevImage img{(uint32_t *)(hb + o_r4), (uint16_t *)(hb + o_sr), (uint32_t *)(hb + o_lr),
-                     (uint16_t *)(hb + o_srp), (uint16_t *)(hb + o_sap), (uint16_t *)(hb + o_scp),
+                     (uint16_t *)(hb + o_srp),
                      (float *)(hb + o_rsc), (uint16_t *)(hb + o_sa),
                      (uint16_t *)(hb + o_sc), (float *)(hb + o_sb), (float *)(hb + o_sd)};
     relayout(s, A5, sA, sB, R4, sR, C8, sC, sD, img,
@@ -294,8 +293,6 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->dev.n_cu = n_cu > 0 ? n_cu : 1;
     h->dev.srp = (const uint16_t *)(db + o_srp);
     h->dev.rsc = (const float *)(db + o_rsc);
-    h->dev.sap = (const uint16_t *)(db + o_sap);
-    h->dev.scp = (const uint16_t *)(db + o_scp);
     h->dev.sa = (const uint16_t *)(db + o_sa);
     h->dev.sc = (const uint16_t *)(db + o_sc);
     h->dev.b8 = (const int8_t *)(db + o_b8);

@@ -41,8 +41,6 @@
 //       residual scale lies in [2^14, 2^15); the large-M kernel turns each
 //       code q into the fp16 value q sR 2^(e_r - 10) with one fused
 //       multiply-add.
-//  sap, scp uint16 [nvb*16]          sA * 2^e_v and sC * 2^e_v in fp16, e_v
-//       per row such that the row's largest of sR, sA, sC lies in [1, 2).
 //  rsc  float  [nvb*16]              2^(10 - e_r) per row.
 //  sa, sc  uint16 [nvb*16]           fp16 row scales of A5 and C8.
 //  b8   int8   [k][d], sb float [k]  right core factor and its row scales.
@@ -93,8 +91,6 @@ struct DevHead {
     const uint16_t *sr;
     const uint32_t *lr;
     const uint16_t *srp;
-    const uint16_t *sap;
-    const uint16_t *scp;
     const float *rsc;
     const uint16_t *sa;
     const uint16_t *sc;
@@ -157,8 +153,6 @@ struct HostDevImage {
     uint16_t *sr;
     uint32_t *lr;
     uint16_t *srp;
-    uint16_t *sap;
-    uint16_t *scp;
     float *rsc;
     uint16_t *sa;
     uint16_t *sc;

@@ -92,15 +92,8 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
             const bool live = row < V;
             for (int64_t c = 0; c < G; ++c)
                 o.sr[(vb * G + c) * kVB + i] = live ? sR[row * G + c] : 0;
-            // power-of-two rescale of the row's scales for the fp16 path
-            const float sa = (live && k > 0) ? half_to_float(sA[row]) : 0.f;
-            const float sc = (live && r > 0) ? half_to_float(sC[row]) : 0.f;
-            float mx = std::max(std::fabs(sa), std::fabs(sc));
-            for (int64_t c = 0; live && c < G; ++c)
-                mx = std::max(mx, std::fabs(half_to_float(sR[row * G + c])));
-            const int e = (mx > 0.f && std::isfinite(mx)) ? -std::ilogb(mx) : 0;
-            // the residual scales on their own: the row's largest into
-            // [2^14, 2^15)
+            // power-of-two rescale of the residual scales for the fp16 path:
+            // the row's largest into [2^14, 2^15)
             float mr = 0.f;
             for (int64_t c = 0; live && c < G; ++c)
                 mr = std::max(mr, std::fabs(half_to_float(sR[row * G + c])));
@@ -108,8 +101,6 @@ void relayout_blocks(const Shape &s, const int8_t *A5, const uint16_t *sA, const
             for (int64_t c = 0; c < G; ++c)
                 o.srp[(vb * G + c) * kVB + i] =
                     live ? float_to_half(std::ldexp(half_to_float(sR[row * G + c]), er + 14)) : 0;
-            o.sap[row] = float_to_half(std::ldexp(sa, e));
-            o.scp[row] = float_to_half(std::ldexp(sc, e));
             o.rsc[row] = std::ldexp(1.0f, 10 - er);
             o.sa[row] = (live && k > 0) ? sA[row] : 0;
             o.sc[row] = (live && r > 0) ? sC[row] : 0;

@@ -13,9 +13,10 @@
 // (global_load_lds), double-buffered with one barrier per stage.
 //
 // One accumulator and one MFMA type (v_mfma_f32_16x16x32_f16) for all three
-// terms, in three phases.  With e_v the row's scale exponent (layout.hpp)
-// and f_m a per-hidden-state power of two (prep_lds_kernel):
-//   1. residual: B = q x (sR 2^e_v), rounded once to fp16 (relative error at
+// terms, in three phases.  With e_r the exponent that puts the row's largest
+// residual scale into [2^14, 2^15) (layout.hpp) and f_m a per-hidden-state
+// power of two (prep_lds_kernel):
+//   1. residual: B = q x (sR 2^(e_r - 10)), rounded once to fp16 (relative error at
 //      most 2^-12 of this, the smallest, term; q and the power-of-two rescale
 //      are exact), A = X 2^f_m in fp16 (exact for every element within 2^29
 //      of the row's largest operand);
