@@ -22,6 +22,10 @@ forward  dense fp64 W_hat (eq 6) and logits (eq 7), first-index argmax
 packer   tiny-head construction (eqs 2-5): damped metric, core, SC4 residual,
          activation-metric correction, INT8 factors
 naive    ctypes loader for naive.c, an independent triple-loop forward in C
+softmax  log-normaliser lse = log sum_v exp(logits) and cross-entropy
+         lse - logit[target] of the logits (abstract and section 1: the
+         logits feed the softmax; the head is judged by cross-entropy and
+         perplexity)
 
 Parity pins (what each function is checked against, in tests/):
   quant   -- closed-form bounds |x - s q| <= s/2, ranges, idempotence, and
@@ -31,6 +35,9 @@ Parity pins (what each function is checked against, in tests/):
   forward -- the independent C triple loop, one-hot closed forms, special
              cases reducing to plain integer matrix products, a hand-worked
              example in tests/golden/forward_example.txt
+  softmax -- closed forms (equal logits: ln V; V = 1; two-way softplus),
+             shift invariance, softmax sums to one, math.fsum brute force on
+             tiny rows, scipy's logsumexp at overflow-prone magnitudes
   packer  -- Eckart-Young-Mirsky tail energy, brute force over random and
              grid rank-r candidates, the eigenvector route, the p = 1/2
              identity with eq 1, the isotropic (C = I) reduction
