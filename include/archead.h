@@ -173,6 +173,41 @@ archead_status archead_forward_timed(archead_t h, int64_t M, const void *X, floa
                                      void *ev_before, void *ev_after);
 
 /*
+ * archead_forward_ce -- the forward plus the softmax log-normaliser and
+ * the cross-entropy of each hidden state's logits, reduced inside the
+ * vocabulary-tile pass (the logits need not be written).  The ARCHead
+ * pages (abstract and section 1) note that the head's logits go straight
+ * into the softmax and judge the head by the cross-entropy it adds and by
+ * relative perplexity = exp(mean cross-entropy); in natural logarithms:
+ *   lse[m] = log sum_v exp(logits[m, v])
+ *   nll[m] = lse[m] - logits[m, targets[m]]
+ *
+ * targets  DEVICE int32 M, the target row of each hidden state, or NULL
+ *          (then nll must be NULL too).  A target outside [0, V) gives
+ *          nll[m] = NaN; it is not an error.
+ * logits   DEVICE fp32 M x V, or NULL to skip writing the logits.
+ * argmax   DEVICE int32 M (as archead_forward_argmax), or NULL.
+ * lse      DEVICE fp32 M, written in full; NULL -> ARCHEAD_EINVAL.
+ * nll      DEVICE fp32 M, written in full, or NULL (with targets NULL).
+ *          targets and nll not both given or both NULL -> ARCHEAD_EINVAL.
+ * Other arguments, ownership and stream behaviour as archead_forward.
+ * Numerics: lse and nll are taken from the same fp32 logits the forward
+ * writes; exponentials and sums run in fp32 against each tile's maximum
+ * (no overflow for any finite logits), so lse equals the log-normaliser of
+ * those logits up to fp32 rounding of the exponentials and their sums.
+ * NaN or infinite logits make lse and nll of that row unspecified.
+ */
+archead_status archead_forward_ce(archead_t h, int64_t M, const void *X, const int32_t *targets,
+                                  float *logits, int32_t *argmax, float *lse, float *nll,
+                                  void *hip_stream);
+
+/* archead_forward_ce_path -- archead_forward_ce with the vocabulary-tile
+ * kernel family forced (archead_path); an unknown path -> ARCHEAD_EINVAL. */
+archead_status archead_forward_ce_path(archead_t h, int64_t M, const void *X, const int32_t *targets,
+                                       float *logits, int32_t *argmax, float *lse, float *nll,
+                                       int path, void *hip_stream);
+
+/*
  * archead_packed_bytes -- eq 10 of the ARCHead paper: the sum over the
  * registered packed buffers of numel x element size (A5 counted at 5 bits,
  * R4 at 4 bits, int8 fields at 8, scales at 16; each buffer rounded up to a

@@ -30,6 +30,8 @@ SIGNATURES = {
     "archead_forward_argmax": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP]),
     "archead_forward_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP]),
     "archead_forward_timed": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP]),
+    "archead_forward_ce": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "archead_forward_ce_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int, _VP]),
     "archead_packed_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_free": (ctypes.c_int, [_VP]),
@@ -148,6 +150,40 @@ class PackedHead:
             p, _stream_handle(stream), ctypes.c_void_p(ev_before.cuda_event),
             ctypes.c_void_p(ev_after.cuda_event))
         _check(st, "archead_forward_timed")
+
+    def forward_ce_into(self, X, targets, logits, argmax, lse, nll, path: str | int = "auto",
+                        stream=None):
+        """Enqueue the forward with the log-normaliser lse (and, with int32
+        targets, the cross-entropy nll) into preallocated torch tensors;
+        targets / nll, logits and argmax may be None."""
+        p = PATHS[path] if isinstance(path, str) else int(path)
+
+        def ptr(t):
+            return None if t is None else ctypes.c_void_p(t.data_ptr())
+        st = load_library().archead_forward_ce_path(
+            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()), ptr(targets), ptr(logits),
+            ptr(argmax), ptr(lse), ptr(nll), p, _stream_handle(stream))
+        _check(st, "archead_forward_ce_path")
+
+    def forward_ce(self, X, targets=None, want_logits: bool = False, want_argmax: bool = False,
+                   path: str | int = "auto", stream=None):
+        """Returns (lse fp32 M, nll fp32 M or None, logits or None, argmax or None)."""
+        import torch
+        if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("X must hold bf16 values")
+        if X.dim() != 2 or X.shape[1] != self.d or not X.is_contiguous():
+            raise ValueError(f"X must be a contiguous M x {self.d} tensor")
+        M = X.shape[0]
+        if targets is not None and (targets.dtype != torch.int32 or targets.shape != (M,)
+                                    or not targets.is_contiguous()):
+            raise ValueError("targets must be a contiguous int32 tensor of M entries")
+        dev = X.device
+        lse = torch.empty((M,), dtype=torch.float32, device=dev)
+        nll = torch.empty((M,), dtype=torch.float32, device=dev) if targets is not None else None
+        logits = torch.empty((M, self.V), dtype=torch.float32, device=dev) if want_logits else None
+        argmax = torch.empty((M,), dtype=torch.int32, device=dev) if want_argmax else None
+        self.forward_ce_into(X, targets, logits, argmax, lse, nll, path=path, stream=stream)
+        return lse, nll, logits, argmax
 
     def forward(self, X, want_logits: bool = True, want_argmax: bool = False,
                 path: str | int = "auto", stream=None):

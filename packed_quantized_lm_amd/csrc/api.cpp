@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, sync, keys, colflag, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, lsep, tl, sync, keys, colflag, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -108,6 +108,10 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(lds_stages(s)) * 16 * 4);
     L.part = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
+    L.lsep = off;
+    off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
+    L.tl = off;
+    off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * 4);
     L.sync = off;
     off = align_up(off + kSyncWords * 4);
     L.keys = off;
@@ -163,6 +167,10 @@ Work make_work(archead_t h, int64_t M)
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
     w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
+    w.lsep = (uint64_t *)(b + L.lsep);
+    w.tl = (float *)(b + L.tl);
+    w.want_lse = 0;
+    w.targets = nullptr;
     w.sync = (uint32_t *)(b + L.sync);
     w.keys = (uint64_t *)(b + L.keys);
     w.colflag = (uint32_t *)(b + L.colflag);
@@ -334,7 +342,8 @@ archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream)
 
 static archead_status forward_impl(archead_t h, int64_t M, const void *X, float *logits,
                                    int32_t *argmax, int path, void *hip_stream, hipEvent_t ev0,
-                                   hipEvent_t ev1)
+                                   hipEvent_t ev1, const int32_t *targets = nullptr,
+                                   float *lse = nullptr, float *nll = nullptr)
 {
     g_err.clear();
     if (!live(h))
@@ -347,8 +356,12 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
         return fail(ARCHEAD_EINVAL, "unknown path");
     if (M == 0)
         return ARCHEAD_OK;
-    if (!logits && !argmax)
-        return fail(ARCHEAD_EINVAL, "logits and argmax are both NULL");
+    if (!logits && !argmax && !lse)
+        return fail(ARCHEAD_EINVAL, "logits, argmax and lse are all NULL");
+    if ((targets != nullptr) != (nll != nullptr))
+        return fail(ARCHEAD_EINVAL, "targets and nll must be given together");
+    if (nll && !lse)
+        return fail(ARCHEAD_EINVAL, "nll needs lse");
     if (!X)
         return fail(ARCHEAD_EINVAL, "X is NULL");
     if (((uintptr_t)X) % 16)
@@ -370,11 +383,13 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
                             (chosen == ARCHEAD_PATH_SKINNY && decode_ok(h->dev, M, true));
 
     Work w = make_work(h, M);
+    w.want_lse = lse ? 1 : 0;
+    w.targets = targets;
     const uint16_t *Xb = (const uint16_t *)X;
     if (one_launch) { // projection, tiles and argmax
         if (ev0)
             HIP_TRY(hipEventRecord(ev0, st));
-        HIP_TRY(launch_decode(h->dev, w, Xb, logits, argmax, chosen == ARCHEAD_PATH_SKINNY, st));
+        HIP_TRY(launch_decode(h->dev, w, Xb, logits, argmax, lse, nll, chosen == ARCHEAD_PATH_SKINNY, st));
         if (ev1)
             HIP_TRY(hipEventRecord(ev1, st));
         return ARCHEAD_OK;
@@ -393,9 +408,9 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
         HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
-    if (argmax) {
+    if (argmax || lse) {
         const int64_t n_part = chosen == ARCHEAD_PATH_LDS ? lds_n_part(h->dev, M) : skinny_n_part(h->dev, M);
-        HIP_TRY(launch_argmax(w, n_part, argmax, st));
+        HIP_TRY(launch_finish(w, n_part, h->s.V, argmax, lse, nll, st));
     }
     return ARCHEAD_OK;
 }
@@ -436,6 +451,23 @@ archead_status archead_forward_argmax(archead_t h, int64_t M, const void *X, flo
         return ARCHEAD_EINVAL;
     }
     return archead_forward_path(h, M, X, logits, argmax, ARCHEAD_PATH_AUTO, hip_stream);
+}
+
+archead_status archead_forward_ce_path(archead_t h, int64_t M, const void *X, const int32_t *targets,
+                                      float *logits, int32_t *argmax, float *lse, float *nll, int path,
+                                      void *hip_stream)
+{
+    if (!lse) {
+        g_err = "lse is NULL";
+        return ARCHEAD_EINVAL;
+    }
+    return forward_impl(h, M, X, logits, argmax, path, hip_stream, nullptr, nullptr, targets, lse, nll);
+}
+
+archead_status archead_forward_ce(archead_t h, int64_t M, const void *X, const int32_t *targets,
+                                  float *logits, int32_t *argmax, float *lse, float *nll, void *hip_stream)
+{
+    return archead_forward_ce_path(h, M, X, targets, logits, argmax, lse, nll, ARCHEAD_PATH_AUTO, hip_stream);
 }
 
 archead_status archead_packed_bytes(archead_t h, uint64_t *bytes)

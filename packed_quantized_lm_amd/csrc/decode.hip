@@ -133,6 +133,7 @@ struct DecodeArgs {
     const uint16_t *X;
     float *logits;   // M x V, may be null
     int32_t *argmax; // M, may be null
+    float *lse, *nll; // M each, may be null (lse with a.w.want_lse; nll with targets)
     int64_t nvb, nkc, G, na, nlr;
     int gsteps;
     int ntask;       // k + r projection columns
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     constexpr int NV = decode_nv(MF);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MF];
+    __shared__ LsePart lred[4][MF];
     const uint16_t *s_sr = (const uint16_t *)smem;
     const uint16_t *s_x = (const uint16_t *)(smem + a.lds_x);
 
@@ -921,6 +923,37 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 red[wv][m] = kk;
         }
     }
+    // the wave's (max, sum exp) per hidden state over its live rows (lanes
+    // 0..15 hold rows lr of the wave's v-blocks), and the target's logit from
+    // the lane that holds it, complete before the workgroup is counted
+    if (a.w.want_lse) {
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            const int32_t tgt = a.w.targets ? a.w.targets[m] : -1;
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+                if (row < V) {
+                    mx = fmaxf(mx, yv[v][m]);
+                    if (row == tgt && lane < 16)
+                        __hip_atomic_store(a.w.tl + m, yv[v][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            mx = max16(mx);
+            float sx = 0.f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+                if (row < V)
+                    sx += exp_le0(yv[v][m] - mx);
+            }
+            sx = sum16(sx);
+            if (lane == 0)
+                lred[wv][m] = LsePart{mx, sx};
+        }
+        wait_vm_all();
+    }
     // every wave of the workgroup is past its last use of the counters and
     // has its keys in LDS
     __syncthreads();
@@ -938,6 +971,11 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     if (a.argmax && lane < MF) {
         const uint64_t kk = umax64(umax64(red[0][lane], red[1][lane]), umax64(red[2][lane], red[3][lane]));
         __hip_atomic_fetch_max(a.w.keys + slot * 32 + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.w.want_lse && lane < MF) {
+        const LsePart p = lse_merge(lse_merge(lred[0][lane], lred[1][lane]), lse_merge(lred[2][lane], lred[3][lane]));
+        __hip_atomic_store(a.w.lsep + (int64_t)lane * a.nwg + bid, lse_bits(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vm_all();
     uint32_t prev = 0;
@@ -962,6 +1000,27 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     kk = umax64(kk, shfl_xor_u64(kk, off));
                 if (lane < MF)
                     a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+            }
+            if (a.w.want_lse) {
+                // every workgroup's summary is final once every slot is counted
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    LsePart p{-__builtin_inff(), 0.f};
+                    for (int i = lane; i < a.nwg; i += 64)
+                        p = lse_merge(p, lse_unbits(__hip_atomic_load(a.w.lsep + (int64_t)m * a.nwg + i,
+                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+                    p = lse_merge64(p);
+                    if (lane == 0) {
+                        const float L = p.mx + logf(p.s);
+                        a.lse[m] = L;
+                        if (a.nll) {
+                            const int32_t t = a.w.targets[m];
+                            a.nll[m] = (t >= 0 && (int64_t)t < V)
+                                           ? L - __hip_atomic_load(a.w.tl + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                           : __builtin_nanf("");
+                        }
+                    }
+                }
             }
             if (lane == 0) {
                 __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1037,7 +1096,7 @@ static DecodeKernel decode_kernel(const DevHead &h, int64_t M, bool mx)
 bool decode_ok(const DevHead &h, int64_t M, bool mx) { return decode_kernel(h, M, mx) != nullptr; }
 
 hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
-                         bool mx, hipStream_t st)
+                         float *lse, float *nll, bool mx, hipStream_t st)
 {
     const DecodeKernel kern = decode_kernel(h, w.M, mx);
     if (!kern)
@@ -1049,6 +1108,8 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     a.X = X;
     a.logits = logits;
     a.argmax = argmax;
+    a.lse = lse;
+    a.nll = nll;
     a.nvb = h.s.nvb();
     a.nkc = h.s.nkc();
     a.G = h.s.G();
@@ -1062,6 +1123,8 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     // free (two workgroups per CU), at least one column per wave
     const int64_t spare = int64_t(2) * h.n_cu - a.nwg;
     a.ntwg = spare > 0 ? (int)std::min<int64_t>(spare, (a.ntask + 3) / 4) : 0;
+    if (w.want_lse && (!lse || int64_t(a.nwg) * w.M > w.part_cap))
+        return hipErrorInvalidValue; // the summaries do not fit the workspace
     a.lds_sa = L.sa;
     a.lds_x = L.x;
     a.lds_ts = L.ts;

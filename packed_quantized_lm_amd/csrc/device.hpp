@@ -196,4 +196,60 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// ---- log-sum-exp partials ---------------------------------------------------
+// A set of logits is summarised by (mx, s): its maximum and the sum of
+// exp(y - mx) over it; the empty set is (-inf, 0).  Two summaries merge
+// exactly in real arithmetic, so the tiles of a row can be reduced in any
+// order.  exp(x) for x <= 0 is taken as 2^(x log2 e) on the hardware base-2
+// exponential.
+constexpr float kLog2e = 1.44269504088896340736f;
+__device__ __forceinline__ float exp_le0(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+struct LsePart {
+    float mx, s;
+};
+
+__device__ __forceinline__ LsePart lse_merge(LsePart a, LsePart b)
+{
+    const float mx = fmaxf(a.mx, b.mx);
+    if (mx == -__builtin_inff())
+        return {mx, 0.f};
+    return {mx, a.s * exp_le0(a.mx - mx) + b.s * exp_le0(b.mx - mx)};
+}
+
+// a summary as one 64-bit word (for the single-launch path's atomic stores)
+__device__ __forceinline__ uint64_t lse_bits(LsePart p)
+{
+    return ((uint64_t)__float_as_uint(p.s) << 32) | (uint64_t)__float_as_uint(p.mx);
+}
+__device__ __forceinline__ LsePart lse_unbits(uint64_t b)
+{
+    return {__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
+// max / sum over the 16 lanes l ^ 1, ..., l ^ 8 (one MFMA column group)
+__device__ __forceinline__ float max16(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 1));
+    x = fmaxf(x, __shfl_xor(x, 2));
+    x = fmaxf(x, __shfl_xor(x, 4));
+    return fmaxf(x, __shfl_xor(x, 8));
+}
+__device__ __forceinline__ float sum16(float x)
+{
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    return x + __shfl_xor(x, 8);
+}
+
+// merge of the summaries held by all 64 lanes (every lane gets the result)
+__device__ __forceinline__ LsePart lse_merge64(LsePart p)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+        p = lse_merge(p, LsePart{__shfl_xor(p.mx, off), __shfl_xor(p.s, off)});
+    return p;
+}
+
 } // namespace archead

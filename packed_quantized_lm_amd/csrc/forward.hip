@@ -407,31 +407,77 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
 // a3: top-1 reduction across vocabulary tiles.  Keys order by value, then by
 // lower index, so the maximum key is the first index of the maximum logit.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void argmax_kernel(const uint64_t *part, int64_t n_part,
-                                                     int32_t *out, int64_t M)
+struct FinishArgs {
+    const uint64_t *part; // [M][n_part] argmax keys
+    const uint64_t *lsep; // [M][n_part] log-sum-exp summaries
+    int64_t n_part, M, V;
+    int32_t *argmax;        // may be null
+    float *lse, *nll;       // may be null (nll needs targets)
+    const int32_t *targets; // [M]
+    const float *tl;        // [M] target logits
+};
+
+// One workgroup per row m: the first index of the largest logit, and
+// lse = mx + log s over the merged summaries; nll = lse - the target's
+// logit, NaN for a target outside [0, V).
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs a)
 {
     __shared__ uint64_t red[4];
+    __shared__ LsePart lred[4];
     const int64_t m = blockIdx.x;
-    if (m >= M)
+    if (m >= a.M)
         return;
-    uint64_t key = 0;
-    for (int64_t i = threadIdx.x; i < n_part; i += 256)
-        key = umax64(key, part[m * n_part + i]);
-    for (int off = 32; off >= 1; off >>= 1)
-        key = umax64(key, shfl_xor_u64(key, off));
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = key;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (a.argmax) { // uniform
+        uint64_t key = 0;
+        for (int64_t i = threadIdx.x; i < a.n_part; i += 256)
+            key = umax64(key, a.part[m * a.n_part + i]);
+        for (int off = 32; off >= 1; off >>= 1)
+            key = umax64(key, shfl_xor_u64(key, off));
+        if (lane == 0)
+            red[wv] = key;
+    }
+    if (a.lse) { // uniform
+        LsePart p{-__builtin_inff(), 0.f};
+        for (int64_t i = threadIdx.x; i < a.n_part; i += 256)
+            p = lse_merge(p, lse_unbits(a.lsep[m * a.n_part + i]));
+        p = lse_merge64(p);
+        if (lane == 0)
+            lred[wv] = p;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        key = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-        out[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+    if (threadIdx.x != 0)
+        return;
+    if (a.argmax) {
+        const uint64_t key = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+        a.argmax[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+    }
+    if (a.lse) {
+        const LsePart p = lse_merge(lse_merge(lred[0], lred[1]), lse_merge(lred[2], lred[3]));
+        const float L = p.mx + logf(p.s);
+        a.lse[m] = L;
+        if (a.nll) {
+            const int32_t t = a.targets[m];
+            a.nll[m] = (t >= 0 && (int64_t)t < a.V) ? L - a.tl[m] : __builtin_nanf("");
+        }
     }
 }
 
-hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st)
+hipError_t launch_finish(const Work &w, int64_t n_part, int64_t V, int32_t *argmax, float *lse, float *nll,
+                         hipStream_t st)
 {
-    hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)w.M), dim3(256), 0, st, w.part, n_part,
-                       argmax, w.M);
+    FinishArgs a;
+    a.part = w.part;
+    a.lsep = w.lsep;
+    a.n_part = n_part;
+    a.M = w.M;
+    a.V = V;
+    a.argmax = argmax;
+    a.lse = lse;
+    a.nll = nll;
+    a.targets = w.targets;
+    a.tl = w.tl;
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)w.M), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

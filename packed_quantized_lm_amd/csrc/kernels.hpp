@@ -48,12 +48,17 @@ constexpr int64_t kLdsMinM = 128;
 // workgroup.  mx = false: VALU bf16-pair dot products (a2-G); mx = true:
 // the same stream with the products on the matrix cores (a2-S, g = 128,
 // M = 1).
+// With w.want_lse the last workgroup also merges every workgroup's
+// log-sum-exp summary into lse (and nll, with w.targets).
 // decode_ok tells whether a shape and M are supported.
 bool decode_ok(const DevHead &h, int64_t M, bool mx);
 hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
-                         bool mx, hipStream_t st);
+                         float *lse, float *nll, bool mx, hipStream_t st);
 
-// a3: reduce the argmax partial keys of each row to an index.
-hipError_t launch_argmax(const Work &w, int64_t n_part, int32_t *argmax, hipStream_t st);
+// a3 (and the log-normaliser): reduce each row's argmax partial keys to an
+// index (argmax not null) and its log-sum-exp summaries to lse and, with
+// targets, nll = lse - the target's logit (lse not null).
+hipError_t launch_finish(const Work &w, int64_t n_part, int64_t V, int32_t *argmax, float *lse, float *nll,
+                         hipStream_t st);
 
 } // namespace archead

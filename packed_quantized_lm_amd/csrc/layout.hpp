@@ -124,6 +124,12 @@ struct Work {
     uint32_t *sync;    // [kSyncWords]
     uint64_t *keys;    // [kKeyWords]
     uint32_t *colflag; // [k + r] call number + 1 once column i of t / s is published
+    // log-normaliser and cross-entropy of the logits (per call):
+    int want_lse;           // write (max, sum exp) summaries beside the argmax keys
+    const int32_t *targets; // [M] target row per hidden state, may be null
+    uint64_t *lsep;         // [M][n_part] summaries (LsePart as 64 bits); the
+                            // single-launch path uses [M][workgroups]
+    float *tl;              // [M] the logit of each hidden state's target row
 };
 
 constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MT * 16];
+    __shared__ LsePart lred[4][MT * 16];
     uint16_t *s_sr = (uint16_t *)smem;
     float *s_xs = (float *)(smem + a.lds_xs);
     uint16_t *s_x = (uint16_t *)(smem + a.lds_x);
@@ -446,25 +447,60 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
             }
             key[mt][i] = k;
         }
-    if (!a.want_argmax)
+    if (!a.want_argmax && !a.w.want_lse)
         return; // uniform across the grid
-    for (int mt = 0; mt < MT; ++mt)
-        for (int i = 0; i < 4; ++i) {
-            uint64_t k = key[mt][i];
-            k = umax64(k, shfl_xor_u64(k, 1));
-            k = umax64(k, shfl_xor_u64(k, 2));
-            k = umax64(k, shfl_xor_u64(k, 4));
-            k = umax64(k, shfl_xor_u64(k, 8));
-            if (lr == 0)
-                red[wv][mt * 16 + 4 * lq + i] = k;
-        }
+    if (a.want_argmax)
+        for (int mt = 0; mt < MT; ++mt)
+            for (int i = 0; i < 4; ++i) {
+                uint64_t k = key[mt][i];
+                k = umax64(k, shfl_xor_u64(k, 1));
+                k = umax64(k, shfl_xor_u64(k, 2));
+                k = umax64(k, shfl_xor_u64(k, 4));
+                k = umax64(k, shfl_xor_u64(k, 8));
+                if (lr == 0)
+                    red[wv][mt * 16 + 4 * lq + i] = k;
+            }
+    if (a.w.want_lse) {
+        // the wave's (max, sum exp) per hidden state over its live rows, and
+        // the logit of the target row where this lane holds it
+        for (int mt = 0; mt < MT; ++mt)
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = mbase + mt * 16 + 4 * lq + i;
+                const int32_t tgt = (a.w.targets && m < M) ? a.w.targets[m] : -1;
+                float mx = -__builtin_inff();
+                for (int v = 0; v < NV; ++v) {
+                    const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+                    if (row < V && m < M) {
+                        mx = fmaxf(mx, acc[v][mt][i]);
+                        if (row == tgt)
+                            a.w.tl[m] = acc[v][mt][i];
+                    }
+                }
+                mx = max16(mx);
+                float sx = 0.f;
+                for (int v = 0; v < NV; ++v) {
+                    const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+                    if (row < V && m < M)
+                        sx += exp_le0(acc[v][mt][i] - mx);
+                }
+                sx = sum16(sx);
+                if (lr == 0)
+                    lred[wv][mt * 16 + 4 * lq + i] = LsePart{mx, sx};
+            }
+    }
     __syncthreads();
     if (threadIdx.x < MT * 16) {
         const int64_t m = mbase + threadIdx.x;
-        const uint64_t k = umax64(umax64(red[0][threadIdx.x], red[1][threadIdx.x]),
-                                  umax64(red[2][threadIdx.x], red[3][threadIdx.x]));
-        if (m < M)
+        if (m < M && a.want_argmax) {
+            const uint64_t k = umax64(umax64(red[0][threadIdx.x], red[1][threadIdx.x]),
+                                      umax64(red[2][threadIdx.x], red[3][threadIdx.x]));
             a.w.part[m * a.w.n_part + vrange] = k;
+        }
+        if (m < M && a.w.want_lse) {
+            const LsePart p = lse_merge(lse_merge(lred[0][threadIdx.x], lred[1][threadIdx.x]),
+                                        lse_merge(lred[2][threadIdx.x], lred[3][threadIdx.x]));
+            a.w.lsep[m * a.w.n_part + vrange] = lse_bits(p);
+        }
     }
 }
 

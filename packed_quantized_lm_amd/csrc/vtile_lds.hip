@@ -544,22 +544,31 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     ARCHEAD_LDS_PHASE(p2, nst, compute_a5)
 #undef ARCHEAD_LDS_PHASE
 
-    // back to logits units; write logits and the workgroup's top-1 keys
+    // back to logits units; write logits, the workgroup's top-1 keys and
+    // its (max, sum exp) summaries.  The summaries go to the first stage
+    // buffer: every stage has been consumed and no fill is in flight.
+    LsePart *const s_lred = (LsePart *)s_buf0; // [kLW][kLRows]
+    const bool want_lse = a.w.want_lse != 0;   // uniform across the grid
 #pragma unroll
     for (int mb = 0; mb < kLMB; ++mb) {
         const f32x4 fi = *(const f32x4 *)(s_fm + kLRows + mb * 16 + 4 * lq);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = mbase + mb * 16 + 4 * lq + i;
+            const int32_t tgt = (want_lse && a.w.targets && m < M) ? a.w.targets[m] : -1;
             uint64_t k = 0;
+            float y[kLVB], mx = -__builtin_inff();
 #pragma unroll
             for (int v = 0; v < kLVB; ++v) {
                 const int64_t row = (vb0 + v) * kVB + lr;
-                const float y = T[mb][v][i] * pa(v) * fi[i];
+                y[v] = T[mb][v][i] * pa(v) * fi[i];
                 if (m < M && vb0 + v < nvb && row < V) {
                     if (a.logits)
-                        a.logits[m * V + row] = y;
-                    k = umax64(k, argmax_key(y, (uint32_t)row));
+                        a.logits[m * V + row] = y[v];
+                    k = umax64(k, argmax_key(y[v], (uint32_t)row));
+                    mx = fmaxf(mx, y[v]);
+                    if (row == tgt)
+                        a.w.tl[m] = y[v];
                 }
             }
             if (a.want_argmax) { // uniform across the grid
@@ -570,19 +579,40 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
                 if (lr == 0)
                     s_red[wv * kLRows + mb * 16 + 4 * lq + i] = k;
             }
+            if (want_lse) {
+                mx = max16(mx);
+                float sx = 0.f;
+#pragma unroll
+                for (int v = 0; v < kLVB; ++v) {
+                    const int64_t row = (vb0 + v) * kVB + lr;
+                    if (m < M && vb0 + v < nvb && row < V)
+                        sx += exp_le0(y[v] - mx);
+                }
+                sx = sum16(sx);
+                if (lr == 0)
+                    s_lred[wv * kLRows + mb * 16 + 4 * lq + i] = LsePart{mx, sx};
+            }
         }
     }
-    if (!a.want_argmax)
+    if (!a.want_argmax && !want_lse)
         return;
     __syncthreads();
     if (threadIdx.x < kLRows) {
-        uint64_t k = 0;
-#pragma unroll
-        for (int w = 0; w < kLW; ++w)
-            k = umax64(k, s_red[w * kLRows + threadIdx.x]);
         const int64_t m = mbase + threadIdx.x;
-        if (m < M)
+        if (m < M && a.want_argmax) {
+            uint64_t k = 0;
+#pragma unroll
+            for (int w = 0; w < kLW; ++w)
+                k = umax64(k, s_red[w * kLRows + threadIdx.x]);
             a.w.part[m * a.w.n_part + vr] = k;
+        }
+        if (m < M && want_lse) {
+            LsePart p = s_lred[threadIdx.x];
+#pragma unroll
+            for (int w = 1; w < kLW; ++w)
+                p = lse_merge(p, s_lred[w * kLRows + threadIdx.x]);
+            a.w.lsep[m * a.w.n_part + vr] = lse_bits(p);
+        }
     }
 }
 

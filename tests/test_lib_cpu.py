@@ -31,7 +31,8 @@ def declared_symbols():
 def test_header_declares_the_documented_entry_points():
     syms = declared_symbols()
     for name in ["archead_pack_load", "archead_forward", "archead_forward_argmax",
-                 "archead_forward_path", "archead_forward_timed", "archead_reserve", "archead_packed_bytes",
+                 "archead_forward_path", "archead_forward_timed", "archead_forward_ce",
+                 "archead_forward_ce_path", "archead_reserve", "archead_packed_bytes",
                  "archead_device_bytes", "archead_free", "archead_status_string",
                  "archead_last_error"]:
         assert name in syms
@@ -113,3 +114,14 @@ def test_binding_raises_without_the_library(tmp_path):
             binding.load_library(str(tmp_path / "missing.so"))
         finally:
             binding._lib = binding._lib_backup
+
+
+def test_forward_ce_rejects_missing_outputs_and_bad_handles(lib):
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call fails its checks first
+    # lse is required
+    assert lib.archead_forward_ce(None, 1, buf, None, None, None, None, None, None) == binding.EINVAL
+    assert "lse" in lib.archead_last_error().decode()
+    # a handle that is not live
+    assert lib.archead_forward_ce(None, 1, buf, None, None, None, buf, None, None) == binding.EINVAL
+    assert lib.archead_forward_ce_path(ctypes.c_void_p(12345), 1, buf, None, None, None, buf, None, 0,
+                                       None) == binding.EINVAL
