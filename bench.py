@@ -151,6 +151,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True):
         del cg
     except Exception as e:  # report, do not hide: the direct-launch numbers stand
         log(f"{name}: graph capture failed: {e!r}")
+    ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path)
     del heads
     torch.cuda.synchronize()
     # The events around the kernel add their own overhead to each launch.
@@ -173,7 +174,55 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True):
         "packed_bytes": packed, "vtile_bytes": vb,
         "vtile_GBs": vb / kern_s / 1e9, "step_GBs_over_packed": packed / (best_ms / 1e3 / steps) / 1e9,
         "path_TFLOPs": fl / (best_ms / 1e3 / steps) / 1e12, "steps": steps,
+        "ce": ce,
     }
+
+
+def measure_ce(heads, X, V, M, steps, warmup, per_graph, path):
+    """The same step through archead_forward_ce with the log-normaliser and
+    cross-entropy reduced inside the tile pass and neither logits nor argmax
+    written (the form a perplexity / cross-entropy loop uses): back-to-back
+    launches and graph replays over the same rotated head copies."""
+    import torch
+    copies = len(heads)
+    targets = torch.from_numpy(np.random.default_rng(7).integers(0, V, M).astype(np.int32)).cuda()
+    lse = torch.empty((M,), dtype=torch.float32, device="cuda")
+    nll = torch.empty_like(lse)
+    step = lambda i: heads[i % copies].forward_ce_into(X, targets, None, None, lse, nll, path=path)
+    for i in range(warmup):
+        step(i)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    direct_ms = start.elapsed_time(stop) / steps
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, stream=side):
+            for i in range(per_graph):
+                step(i)
+        torch.cuda.synchronize()
+        cg.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        start.record()
+        for i in range(reps):
+            cg.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(stop) / (reps * per_graph)
+        del cg
+    except Exception as e:
+        log(f"forward_ce graph capture failed: {e!r}")
+    best = min(direct_ms, graph_ms) if graph_ms is not None else direct_ms
+    return {"ms_per_step": best, "direct_ms_per_step": direct_ms, "graph_ms_per_step": graph_ms,
+            "tokens_per_s": M / (best / 1e3), "writes": "lse and nll only (no logits, no argmax)"}
 
 
 def cpu_baseline(name="qwen_m1", budget_s=15.0):
@@ -289,6 +338,7 @@ def main():
                      "kernel_us": head["vtile_us_mean"],
                      "bytes_per_launch": head["vtile_bytes"]},
         "cpu_baseline": cpu,
+        "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]),
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -143,6 +143,11 @@ struct DecodeArgs {
     unsigned lds_sa, lds_x, lds_ts, lds_xs; // byte offsets of the sA/sC, X, t/s and group-sum regions (sr at 0)
 };
 
+// log-sum-exp summaries each lane of the last workgroup loads at once, and
+// the bits of the empty summary (-inf, 0)
+constexpr int kLseBatch = 16;
+constexpr uint64_t kLseEmpty = 0xFF800000u;
+
 // v-blocks per wave: five at M = 1, four at M = 2 (whose accumulators need
 // the registers), with two prefetch pairs at two waves per SIMD
 constexpr int decode_nv(int MF) { return MF == 1 ? 5 : 4; }
@@ -1005,10 +1010,23 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 // every workgroup's summary is final once every slot is counted
 #pragma unroll
                 for (int m = 0; m < MF; ++m) {
+                    // the first 64 kLseBatch summaries with all their loads in
+                    // flight at once (one round trip), any further ones after
+                    const uint64_t *src = a.w.lsep + (int64_t)m * a.nwg;
+                    uint64_t bits[kLseBatch];
+#pragma unroll
+                    for (int j = 0; j < kLseBatch; ++j) {
+                        const int i = lane + 64 * j;
+                        bits[j] = i < a.nwg ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                            : kLseEmpty;
+                    }
                     LsePart p{-__builtin_inff(), 0.f};
-                    for (int i = lane; i < a.nwg; i += 64)
-                        p = lse_merge(p, lse_unbits(__hip_atomic_load(a.w.lsep + (int64_t)m * a.nwg + i,
-                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+#pragma unroll
+                    for (int j = 0; j < kLseBatch; ++j)
+                        p = lse_merge(p, lse_unbits(bits[j]));
+                    for (int i = lane + 64 * kLseBatch; i < a.nwg; i += 64)
+                        p = lse_merge(p, lse_unbits(__hip_atomic_load(src + i, __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT)));
                     p = lse_merge64(p);
                     if (lane == 0) {
                         const float L = p.mx + logf(p.s);
