@@ -205,6 +205,11 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
+    // cross-entropy targets (uniform: scalar loads, complete long before use)
+    int32_t tgt[MF];
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
+        tgt[m] = (a.w.want_lse && a.w.targets) ? a.w.targets[m] : -1;
 
     // ---- a1: column i of t (i < k) or s (i >= k) for every row m, as a
     // bf16 hi/lo pair in lane m ----
@@ -934,14 +939,13 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     if (a.w.want_lse) {
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
-            const int32_t tgt = a.w.targets ? a.w.targets[m] : -1;
             float mx = -__builtin_inff();
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
                 if (row < V) {
                     mx = fmaxf(mx, yv[v][m]);
-                    if (row == tgt && lane < 16)
+                    if (row == tgt[m] && lane < 16)
                         __hip_atomic_store(a.w.tl + m, yv[v][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }

@@ -227,20 +227,30 @@ __device__ __forceinline__ LsePart lse_unbits(uint64_t b)
     return {__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
 }
 
-// max / sum over the 16 lanes l ^ 1, ..., l ^ 8 (one MFMA column group)
+// max / sum over each row of 16 lanes (one MFMA column group), every lane
+// getting the result, with DPP lane moves instead of LDS permutes: swap
+// neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), then -- all
+// four lanes of a quad now equal -- mirror each half row (lane i <- 7 - i)
+// and each row (lane i <- 15 - i), which meet quads and halves pairwise.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowMirror = 0x140, kDppHalfMirror = 0x141;
 __device__ __forceinline__ float max16(float x)
 {
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    return fmaxf(x, __shfl_xor(x, 8));
+    x = fmaxf(x, dpp_move<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_move<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_move<kDppHalfMirror>(x));
+    return fmaxf(x, dpp_move<kDppRowMirror>(x));
 }
 __device__ __forceinline__ float sum16(float x)
 {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    return x + __shfl_xor(x, 8);
+    x += dpp_move<kDppQuadXor1>(x);
+    x += dpp_move<kDppQuadXor2>(x);
+    x += dpp_move<kDppHalfMirror>(x);
+    return x + dpp_move<kDppRowMirror>(x);
 }
 
 // merge of the summaries held by all 64 lanes (every lane gets the result)

@@ -68,6 +68,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MT * 16];
     __shared__ LsePart lred[4][MT * 16];
+    __shared__ int32_t s_tgt[64]; // targets of the m-tile's rows (cross-entropy)
     uint16_t *s_sr = (uint16_t *)smem;
     float *s_xs = (float *)(smem + a.lds_xs);
     uint16_t *s_x = (uint16_t *)(smem + a.lds_x);
@@ -115,6 +116,11 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
             if (i < G * MT * 16)
                 __builtin_amdgcn_global_load_lds((const void *)(a.w.xsneg + grp * Mp + mbase + j),
                                                  (__attribute__((address_space(3))) void *)d0, 4, 0, 0);
+        }
+        if (a.w.want_lse && a.w.targets && wv == 0) { // rows past M repeat the last target
+            const int64_t m = mbase + lane < M ? mbase + lane : M - 1;
+            __builtin_amdgcn_global_load_lds((const void *)(a.w.targets + m),
+                                             (__attribute__((address_space(3))) void *)s_tgt, 4, 0, 0);
         }
         if (XL)
             stage16(a.X, s_x, M * d / 8);
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
         for (int mt = 0; mt < MT; ++mt)
             for (int i = 0; i < 4; ++i) {
                 const int64_t m = mbase + mt * 16 + 4 * lq + i;
-                const int32_t tgt = (a.w.targets && m < M) ? a.w.targets[m] : -1;
+                const int32_t tgt = (a.w.targets && m < M) ? s_tgt[mt * 16 + 4 * lq + i] : -1;
                 float mx = -__builtin_inff();
                 for (int v = 0; v < NV; ++v) {
                     const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;

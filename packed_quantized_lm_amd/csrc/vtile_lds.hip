@@ -321,6 +321,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     __shared__ __attribute__((aligned(16))) uint32_t s_buf1[kLStageWords];
     __shared__ __attribute__((aligned(16))) float s_fm[2 * kLRows]; // 2^f_m, then 2^-f_m
     __shared__ uint64_t s_red[kLW * kLRows];
+    __shared__ int32_t s_tgt[kLRows]; // targets of the tile's rows (cross-entropy)
 
     const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     // wave index as a uniform value, so that everything derived from it
@@ -365,6 +366,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         const int64_t m = mbase + threadIdx.x; // below the prepared row count
         s_fm[threadIdx.x] = a.w.xsc[2 * m + 1];      // 2^f_m
         s_fm[kLRows + threadIdx.x] = a.w.xsc[2 * m]; // 2^-f_m
+        if (a.w.want_lse && a.w.targets)
+            s_tgt[threadIdx.x] = m < a.w.M ? a.w.targets[m] : -1;
     }
 
     // ---- stage fill --------------------------------------------------------
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = mbase + mb * 16 + 4 * lq + i;
-            const int32_t tgt = (want_lse && a.w.targets && m < M) ? a.w.targets[m] : -1;
+            const int32_t tgt = (want_lse && a.w.targets && m < M) ? s_tgt[mb * 16 + 4 * lq + i] : -1;
             uint64_t k = 0;
             float y[kLVB], mx = -__builtin_inff();
 #pragma unroll
