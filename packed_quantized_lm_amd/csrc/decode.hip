@@ -925,10 +925,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
             uint64_t kk = key[m];
-            kk = umax64(kk, shfl_xor_u64(kk, 1));
-            kk = umax64(kk, shfl_xor_u64(kk, 2));
-            kk = umax64(kk, shfl_xor_u64(kk, 4));
-            kk = umax64(kk, shfl_xor_u64(kk, 8));
+            kk = umax16_u64(kk);
             if (lane == 0)
                 red[wv][m] = kk;
         }

@@ -252,6 +252,21 @@ __device__ __forceinline__ float sum16(float x)
     x += dpp_move<kDppHalfMirror>(x);
     return x + dpp_move<kDppRowMirror>(x);
 }
+// the same for the 64-bit argmax keys: the maximum key over each row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_move_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax16_u64(uint64_t k)
+{
+    k = umax64(k, dpp_move_u64<kDppQuadXor1>(k));
+    k = umax64(k, dpp_move_u64<kDppQuadXor2>(k));
+    k = umax64(k, dpp_move_u64<kDppHalfMirror>(k));
+    return umax64(k, dpp_move_u64<kDppRowMirror>(k));
+}
 
 // merge of the summaries held by all 64 lanes (every lane gets the result)
 __device__ __forceinline__ LsePart lse_merge64(LsePart p)

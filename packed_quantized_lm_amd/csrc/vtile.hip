@@ -459,10 +459,7 @@ __global__ __launch_bounds__(256, WIDE ? 2 : (XL ? 3 : (MT == 1 ? 2 : 1))) void 
         for (int mt = 0; mt < MT; ++mt)
             for (int i = 0; i < 4; ++i) {
                 uint64_t k = key[mt][i];
-                k = umax64(k, shfl_xor_u64(k, 1));
-                k = umax64(k, shfl_xor_u64(k, 2));
-                k = umax64(k, shfl_xor_u64(k, 4));
-                k = umax64(k, shfl_xor_u64(k, 8));
+                k = umax16_u64(k);
                 if (lr == 0)
                     red[wv][mt * 16 + 4 * lq + i] = k;
             }

@@ -575,10 +575,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
                 }
             }
             if (a.want_argmax) { // uniform across the grid
-                k = umax64(k, shfl_xor_u64(k, 1));
-                k = umax64(k, shfl_xor_u64(k, 2));
-                k = umax64(k, shfl_xor_u64(k, 4));
-                k = umax64(k, shfl_xor_u64(k, 8));
+                k = umax16_u64(k);
                 if (lr == 0)
                     s_red[wv * kLRows + mb * 16 + 4 * lq + i] = k;
             }
