@@ -47,7 +47,7 @@ def vtile_bytes(V, d, k, r, g, M):
     """Algorithmic HBM bytes of one vocabulary-tile launch: every packed field
     it reads once (R4 4 bits, sR fp16 per group, A5 5 bits, sA, C8 8 bits, sC),
     X read once, logits written once."""
-    per_row = d // 2 + 2 * (d // g) + (5 * k + 7) // 8 + 2 + r + 2
+    per_row = d // 2 + 2 * (d // g) + (5 * k + 7) // 8 + (2 if k else 0) + r + (2 if r else 0)
     return V * per_row + M * d * 2 + M * V * 4
 
 
@@ -278,6 +278,8 @@ def main():
     ap.add_argument("--path", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the naive group-INT4 and SVD8+INT4 heads")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many bytes "
                          "--steps times (calibration of the HBM byte counters)")
@@ -308,6 +310,21 @@ def main():
             s["hbm_frac"] = s["vtile_GBs"] / HBM_PEAK_GBS
             log(json.dumps(s))
             secondary.append(s)
+    # the baseline heads the pages compare against, on the same kernels and
+    # the same rotated-copy timing, beside the packed head's step at that M
+    baselines = []
+    if not args.no_baselines:
+        same_m = {head["M"]: head["ms_per_step"]}
+        same_m.update({s["M"]: s["ms_per_step"] for s in secondary if s["workload"].startswith("qwen")})
+        for name, steps in [("int4_g32_m1", args.steps), ("svd8_int4_m1", args.steps),
+                            ("int4_g32_m2048", max(5, args.steps // 20)),
+                            ("svd8_int4_m2048", max(5, args.steps // 20))]:
+            b = measure(name, steps, max(2, args.warmup // 4), args.copies, path=args.path)
+            b["mfma_frac"] = b["path_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+            b["hbm_frac"] = b["vtile_GBs"] / HBM_PEAK_GBS
+            b["packed_head_ms_per_step_same_M"] = same_m.get(b["M"])
+            log(json.dumps(b))
+            baselines.append(b)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload)
@@ -340,6 +357,7 @@ def main():
         "cpu_baseline": cpu,
         "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]),
         "secondary": secondary,
+        "baselines": baselines,
     }
     print(json.dumps(out), flush=True)
 

@@ -67,14 +67,15 @@ def field_shapes(V: int, d: int, k: int, r: int, g: int) -> dict:
 
     A5 is counted at 5 bits per value (the "5-bit left core factor" of the
     state-dict accounting paragraph), R4 at 4 bits, int8 fields at 8 bits and
-    every scale at 16 bits.
+    every scale at 16 bits.  A head without a core (k = 0) registers no core
+    row scales, and one without a correction (r = 0) none for the correction.
     """
     G = d // g
     return {
         "R4": (V * d, 4), "sR": (V * G, 16),
-        "A5": (V * k, 5), "sA": (V, 16),
+        "A5": (V * k, 5), "sA": (V if k > 0 else 0, 16),
         "B8": (k * d, 8), "sB": (k, 16),
-        "C8": (V * r, 8), "sC": (V, 16),
+        "C8": (V * r, 8), "sC": (V if r > 0 else 0, 16),
         "D8": (r * d, 8), "sD": (r * G, 16),
     }
 

@@ -478,8 +478,11 @@ archead_status archead_packed_bytes(archead_t h, uint64_t *bytes)
     const Shape &s = h->s;
     auto B = [](uint64_t numel, uint64_t bits) { return (numel * bits + 7) / 8; };
     const uint64_t G = s.G();
-    *bytes = B(s.V * s.d, 4) + B(s.V * G, 16) + B(s.V * s.k, 5) + B(s.V, 16) + B(s.k * s.d, 8) +
-             B(s.k, 16) + B(s.V * s.r, 8) + B(s.V, 16) + B(s.r * s.d, 8) + B(s.r * G, 16);
+    // a head without a core (k = 0) or without a correction (r = 0) holds no
+    // row scales for it
+    *bytes = B(s.V * s.d, 4) + B(s.V * G, 16) + B(s.V * s.k, 5) + B(s.k > 0 ? s.V : 0, 16) +
+             B(s.k * s.d, 8) + B(s.k, 16) + B(s.V * s.r, 8) + B(s.r > 0 ? s.V : 0, 16) +
+             B(s.r * s.d, 8) + B(s.r * G, 16);
     return ARCHEAD_OK;
 }
 

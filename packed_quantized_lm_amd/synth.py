@@ -37,8 +37,21 @@ CONFIGS = {
     "qwen_m32": dict(V=151936, d=4096, k=256, r=64, g=128, M=32),
     "qwen_m2048": dict(V=151936, d=4096, k=256, r=64, g=128, M=2048),
     "large_m8": dict(V=262144, d=2560, k=192, r=48, g=128, M=8),
+    # the baselines the pages compare against, at the Qwen head's shape and on
+    # the same kernels: a plain group-INT4 head (no core, no correction) with
+    # the group size whose bytes come closest to the packed head's from below
+    # (g = 32: 350.1 MB against 356.8 MB by eq 10), and "SVD8 + INT4": a rank-256 INT8
+    # low-rank pair (held in the INT8 pair's slot) plus the group-INT4
+    # residual, without the activation-metric correction
+    "int4_g32_m1": dict(V=151936, d=4096, k=0, r=0, g=32, M=1),
+    "int4_g32_m2048": dict(V=151936, d=4096, k=0, r=0, g=32, M=2048),
+    "svd8_int4_m1": dict(V=151936, d=4096, k=0, r=256, g=128, M=1),
+    "svd8_int4_m2048": dict(V=151936, d=4096, k=0, r=256, g=128, M=2048),
 }
-CONFIG_ORDER = ["tiny", "qwen_m1", "qwen_m32", "qwen_m2048", "large_m8"]
+CONFIG_ORDER = ["tiny", "qwen_m1", "qwen_m32", "qwen_m2048", "large_m8",
+                "int4_g32_m1", "int4_g32_m2048", "svd8_int4_m1", "svd8_int4_m2048"]
+# configs that share one head (same seed) and differ only in X
+_HEAD_FAMILIES = {"qwen": 1, "int4_g32": 10, "svd8_int4": 11}
 
 _BASE_SEED = 0xA4C0
 
@@ -132,7 +145,7 @@ def make_config(name: str, M: int | None = None) -> dict:
 
     For every config but "tiny" this returns packed fields + X.  Configs
     qwen_m1 / qwen_m32 / qwen_m2048 share the same head (same seed) and differ
-    only in X.  For "tiny" it returns W, H, X (the oracle packs them).
+    only in X; so do the two sizes of each baseline head.  For "tiny" it returns W, H, X (the oracle packs them).
     """
     c = dict(CONFIGS[name])
     if M is not None:
@@ -144,7 +157,8 @@ def make_config(name: str, M: int | None = None) -> dict:
             out["X"] = to_bf16_bits(hidden_states(_rng(_BASE_SEED, 14, M), M, out["sigma"]))
             out["M"] = M
         return out
-    head_seed = _BASE_SEED + (1 if name.startswith("qwen") else cfg_id)
+    family = name.rsplit("_m", 1)[0]
+    head_seed = _BASE_SEED + _HEAD_FAMILIES.get(family, cfg_id)
     out = random_head(c["V"], c["d"], c["k"], c["r"], c["g"], head_seed)
     if name == "large_m8":
         X = random_x(c["M"], c["d"], _BASE_SEED + cfg_id, n_outliers=8, outlier_factor=30.0)

@@ -66,10 +66,26 @@ def test_packed_bytes_closed_form_equals_sum_of_numel_times_size():
         f = random_small_head(V, d, k, r, g, 1, seed=3)
         total_bits = 0
         for name in ["R4", "sR", "A5", "sA", "B8", "sB", "C8", "sC", "D8", "sD"]:
+            if (name == "sA" and k == 0) or (name == "sC" and r == 0):
+                continue  # no core / no correction: its row scales are not registered
             a = f[name]
             bits = {"R4": 8, "A5": 5}.get(name, a.dtype.itemsize * 8)
             total_bits += (a.size * bits + 7) // 8 * 8
         assert layout.packed_bytes(V, d, k, r, g) * 8 == total_bits
+
+
+def test_plain_group_int4_head_bytes_closed_form():
+    # k = r = 0 leaves a plain group-INT4 head: V d / 2 bytes of nibbles plus
+    # one fp16 scale per (row, group); at the Qwen shape g = 32 is the group
+    # size whose bytes come closest to the packed head's from below
+    V, d = 151936, 4096
+    for g in (32, 64, 128):
+        assert layout.packed_bytes(V, d, 0, 0, g) == V * d // 2 + 2 * V * (d // g)
+    packed = layout.packed_bytes(V, d, 256, 64, 128)
+    assert layout.packed_bytes(V, d, 0, 0, 32) == 350_060_544 <= packed == 356_845_568
+    # SVD8 + INT4: a rank-256 INT8 pair with row scales, group scales on its right factor
+    assert layout.packed_bytes(V, d, 0, 256, 128) == (V * d // 2 + 2 * V * 32 + V * 256 + 2 * V
+                                                      + 256 * d + 2 * 256 * 32)
 
 
 def test_packed_fraction_is_above_the_int4_floor_and_in_the_pages_range():
