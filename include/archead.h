@@ -76,7 +76,9 @@ typedef enum archead_status {
  * projection, the vocabulary tiles and the argmax reduction as separate
  * kernels; both take any M. */
 typedef enum archead_path {
-    ARCHEAD_PATH_AUTO = 0,   /* chosen from M                                  */
+    ARCHEAD_PATH_AUTO = 0,   /* LDS for M >= 128, else SKINNY; GEMV instead at
+                                M = 1 when SKINNY cannot run as one launch
+                                (g != 128) but GEMV can                       */
     ARCHEAD_PATH_GEMV = 1,   /* VALU dot2 GEMV, one launch, M <= 2             */
     ARCHEAD_PATH_SKINNY = 2, /* register-dequantised MFMA, W streamed once     */
     ARCHEAD_PATH_LDS = 3     /* LDS-staged fp16-dequantised MFMA, large M      */

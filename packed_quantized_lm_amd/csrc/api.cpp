@@ -373,8 +373,13 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
         return s;
 
     int chosen = path;
-    if (chosen == ARCHEAD_PATH_AUTO)
+    if (chosen == ARCHEAD_PATH_AUTO) {
         chosen = M >= kLdsMinM ? ARCHEAD_PATH_LDS : ARCHEAD_PATH_SKINNY;
+        // one hidden state on a head the matrix-core single launch does not
+        // take (g != 128): the VALU single launch outruns the streaming kernel
+        if (M == 1 && !decode_ok(h->dev, 1, true) && decode_ok(h->dev, 1, false))
+            chosen = ARCHEAD_PATH_GEMV;
+    }
     if (chosen == ARCHEAD_PATH_GEMV && !decode_ok(h->dev, M, false))
         return fail(ARCHEAD_ESHAPE, "the GEMV path takes M <= " + std::to_string(kDecodeMaxM) +
                                         ", d a multiple of 512 and a head whose staging fits in LDS");
