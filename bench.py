@@ -152,6 +152,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True):
     except Exception as e:  # report, do not hide: the direct-launch numbers stand
         log(f"{name}: graph capture failed: {e!r}")
     ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path)
+    topk = measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits)
     del heads
     torch.cuda.synchronize()
     # The events around the kernel add their own overhead to each launch.
@@ -175,7 +176,60 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True):
         "vtile_GBs": vb / kern_s / 1e9, "step_GBs_over_packed": packed / (best_ms / 1e3 / steps) / 1e9,
         "path_TFLOPs": fl / (best_ms / 1e3 / steps) / 1e12, "steps": steps,
         "ce": ce,
+        "topk": topk,
     }
+
+
+def measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits, K=16):
+    """The same step through archead_forward_topk: logits written, then the K
+    largest of each row selected from them (the step a top-k sampling decode
+    loop runs), back-to-back and from a graph."""
+    import torch
+    if logits is None:
+        logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    copies = len(heads)
+    vals = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    idx = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    step = lambda i: heads[i % copies].forward_topk_into(X, K, logits, vals, idx, path=path)
+    return _time_step(step, steps, warmup, per_graph, M, {"K": K})
+
+
+def _time_step(step, steps, warmup, per_graph, M, extra):
+    import torch
+    for i in range(warmup):
+        step(i)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    direct_ms = start.elapsed_time(stop) / steps
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, stream=side):
+            for i in range(per_graph):
+                step(i)
+        torch.cuda.synchronize()
+        cg.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        start.record()
+        for i in range(reps):
+            cg.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(stop) / (reps * per_graph)
+        del cg
+    except Exception as e:
+        log(f"graph capture failed: {e!r}")
+    best = min(direct_ms, graph_ms) if graph_ms is not None else direct_ms
+    return dict(extra, ms_per_step=best, direct_ms_per_step=direct_ms, graph_ms_per_step=graph_ms,
+                tokens_per_s=M / (best / 1e3))
 
 
 def measure_ce(heads, X, V, M, steps, warmup, per_graph, path):
@@ -356,6 +410,7 @@ def main():
                      "bytes_per_launch": head["vtile_bytes"]},
         "cpu_baseline": cpu,
         "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]),
+        "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]),
         "secondary": secondary,
         "baselines": baselines,
     }

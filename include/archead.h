@@ -210,6 +210,30 @@ archead_status archead_forward_ce_path(archead_t h, int64_t M, const void *X, co
                                        int path, void *hip_stream);
 
 /*
+ * archead_forward_topk -- the forward (logits written) plus the K largest
+ * logits of every hidden state, in order: values[m, 0] is the largest,
+ * equal values by lower vocabulary index (so indices[m, 0] is the argmax of
+ * archead_forward_argmax).  The pages report how often the packed head keeps
+ * the dense head's top-1 token (ARCHead paper section 1, results); the same
+ * ordering over K candidates is what top-k sampling draws from.
+ *
+ * K        1 <= K <= min(16, V); otherwise ARCHEAD_EINVAL.
+ * logits   DEVICE fp32 M x V, written in full (required: the selection
+ *          reads them back after the vocabulary-tile pass).
+ * values   DEVICE fp32 M x K, row-major: values[m, j] = logits[m, indices[m, j]].
+ * indices  DEVICE int32 M x K, row-major.
+ * Other arguments, ownership and stream behaviour as archead_forward.
+ * NaN logits make the order of that row unspecified.
+ */
+archead_status archead_forward_topk(archead_t h, int64_t M, const void *X, int32_t K, float *logits,
+                                    float *values, int32_t *indices, void *hip_stream);
+
+/* archead_forward_topk_path -- archead_forward_topk with the vocabulary-tile
+ * kernel family forced (archead_path); an unknown path -> ARCHEAD_EINVAL. */
+archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, int32_t K, float *logits,
+                                         float *values, int32_t *indices, int path, void *hip_stream);
+
+/*
  * archead_packed_bytes -- eq 10 of the ARCHead paper: the sum over the
  * registered packed buffers of numel x element size (A5 counted at 5 bits,
  * R4 at 4 bits, int8 fields at 8, scales at 16; each buffer rounded up to a

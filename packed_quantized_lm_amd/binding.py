@@ -31,6 +31,9 @@ SIGNATURES = {
     "archead_forward_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP]),
     "archead_forward_timed": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP]),
     "archead_forward_ce": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "archead_forward_topk": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
+    "archead_forward_topk_path": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int,
+                                                 _VP]),
     "archead_forward_ce_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int, _VP]),
     "archead_packed_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
@@ -184,6 +187,26 @@ class PackedHead:
         argmax = torch.empty((M,), dtype=torch.int32, device=dev) if want_argmax else None
         self.forward_ce_into(X, targets, logits, argmax, lse, nll, path=path, stream=stream)
         return lse, nll, logits, argmax
+
+    def forward_topk_into(self, X, K: int, logits, values, indices, path: str | int = "auto", stream=None):
+        """Enqueue the forward plus the K largest logits per row into preallocated
+        torch tensors (logits M x V, values M x K fp32, indices M x K int32)."""
+        p = PATHS[path] if isinstance(path, str) else int(path)
+        st = load_library().archead_forward_topk_path(
+            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()), int(K),
+            ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(values.data_ptr()),
+            ctypes.c_void_p(indices.data_ptr()), p, _stream_handle(stream))
+        _check(st, "archead_forward_topk_path")
+
+    def forward_topk(self, X, K: int, path: str | int = "auto", stream=None):
+        """Returns (values fp32 M x K, indices int32 M x K, logits fp32 M x V)."""
+        import torch
+        M = X.shape[0]
+        logits = torch.empty((M, self.V), dtype=torch.float32, device=X.device)
+        values = torch.empty((M, K), dtype=torch.float32, device=X.device)
+        indices = torch.empty((M, K), dtype=torch.int32, device=X.device)
+        self.forward_topk_into(X, K, logits, values, indices, path=path, stream=stream)
+        return values, indices, logits
 
     def forward(self, X, want_logits: bool = True, want_argmax: bool = False,
                 path: str | int = "auto", stream=None):

@@ -69,7 +69,7 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, lsep, tl, sync, keys, colflag, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, lsep, tl, tkp, sync, keys, colflag, total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -112,6 +112,8 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * max_n_part(s) * 8);
     L.tl = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * 4);
+    L.tkp = off;
+    off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * topk_slices(s.V) * kTopKMax * 8);
     L.sync = off;
     off = align_up(off + kSyncWords * 4);
     L.keys = off;
@@ -169,6 +171,8 @@ Work make_work(archead_t h, int64_t M)
     w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
     w.lsep = (uint64_t *)(b + L.lsep);
     w.tl = (float *)(b + L.tl);
+    w.tkp = (uint64_t *)(b + L.tkp);
+    w.tkp_cap = std::max<int64_t>(h->ws_M, 1) * topk_slices(h->s.V) * kTopKMax;
     w.want_lse = 0;
     w.targets = nullptr;
     w.sync = (uint32_t *)(b + L.sync);
@@ -467,6 +471,30 @@ archead_status archead_forward_ce_path(archead_t h, int64_t M, const void *X, co
         return ARCHEAD_EINVAL;
     }
     return forward_impl(h, M, X, logits, argmax, path, hip_stream, nullptr, nullptr, targets, lse, nll);
+}
+
+archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, int32_t K, float *logits,
+                                        float *values, int32_t *indices, int path, void *hip_stream)
+{
+    g_err.clear();
+    if (!logits || !values || !indices)
+        return fail(ARCHEAD_EINVAL, "logits, values and indices are required");
+    if (!live(h))
+        return fail(ARCHEAD_EINVAL, "invalid or freed handle");
+    if (K < 1 || K > kTopKMax || int64_t(K) > h->s.V)
+        return fail(ARCHEAD_EINVAL, "K must satisfy 1 <= K <= min(" + std::to_string(kTopKMax) + ", V)");
+    archead_status st = forward_impl(h, M, X, logits, nullptr, path, hip_stream, nullptr, nullptr);
+    if (st != ARCHEAD_OK || M == 0)
+        return st;
+    Work w = make_work(h, M);
+    HIP_TRY(launch_topk(w, logits, h->s.V, K, values, indices, (hipStream_t)hip_stream));
+    return ARCHEAD_OK;
+}
+
+archead_status archead_forward_topk(archead_t h, int64_t M, const void *X, int32_t K, float *logits,
+                                    float *values, int32_t *indices, void *hip_stream)
+{
+    return archead_forward_topk_path(h, M, X, K, logits, values, indices, ARCHEAD_PATH_AUTO, hip_stream);
 }
 
 archead_status archead_forward_ce(archead_t h, int64_t M, const void *X, const int32_t *targets,

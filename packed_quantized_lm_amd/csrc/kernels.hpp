@@ -61,4 +61,12 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
 hipError_t launch_finish(const Work &w, int64_t n_part, int64_t V, int32_t *argmax, float *lse, float *nll,
                          hipStream_t st);
 
+// top-k: the K largest logits of each row (larger value first, equal values
+// by lower index), 1 <= K <= min(kTopKMax, V), over logits already written:
+// per-slice selection, then a per-row merge (topk.hip).
+constexpr int kTopKMax = 16;
+int64_t topk_slices(int64_t V);
+hipError_t launch_topk(const Work &w, const float *logits, int64_t V, int K, float *values,
+                       int32_t *indices, hipStream_t st);
+
 } // namespace archead

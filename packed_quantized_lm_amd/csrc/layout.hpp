@@ -130,6 +130,9 @@ struct Work {
     uint64_t *lsep;         // [M][n_part] summaries (LsePart as 64 bits); the
                             // single-launch path uses [M][workgroups]
     float *tl;              // [M] the logit of each hidden state's target row
+    // top-k selection: per (row, 1024-logit slice) the slice's K largest keys
+    uint64_t *tkp;          // [M][slices][K]
+    int64_t tkp_cap;        // uint64 slots in tkp
 };
 
 constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path

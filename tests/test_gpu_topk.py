@@ -1,0 +1,133 @@
+"""GPU parity of the top-k selection (archead_forward_topk) against the CPU
+oracle.  The selection is exact on the logits it reads, so the GPU's indices
+and values must equal oracle/select.py applied to the GPU's own logits,
+bit for bit.  Against the oracle's fp64 logits the chosen rows must be the
+oracle's top K up to near-ties: every chosen row's oracle logit is within the
+logits' tolerance (2e-3 rms) of the oracle's K-th largest, and every row the
+oracle ranks above its K-th largest by more than that is chosen."""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, assert_logits_close, row_rms, say
+from oracle import forward as oracle_forward
+from oracle.select import top_k
+from packed_quantized_lm_amd.synth import make_config, random_small_head
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from packed_quantized_lm_amd import load_library
+    load_library()
+
+
+def load(fields):
+    from packed_quantized_lm_amd import PackedHead
+    return PackedHead(fields)
+
+
+def gpu_topk(head, X_bits, K, path="auto"):
+    import torch
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    v, i, y = head.forward_topk(x_tensor_from_bits(X_bits), K, path=path)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy().astype(np.int64), y.cpu().numpy()
+
+
+def check_exact(v, i, y, K, what):
+    rv, ri = top_k(y, K)
+    assert np.array_equal(i, ri), f"{what}: indices differ from the top-k of the GPU's own logits"
+    assert np.array_equal(v, rv), f"{what}: values differ"
+
+
+def check_oracle(i, ref, K, what, rms=None):
+    rms = row_rms(ref) if rms is None else rms
+    kth = np.sort(ref, axis=1)[:, -K]
+    for m in range(ref.shape[0]):
+        chosen = set(i[m].tolist())
+        assert np.all(ref[m, i[m]] >= kth[m] - TOL * rms[m]), f"{what}: row {m} chose a row far below the K-th"
+        must = np.nonzero(ref[m] > kth[m] + TOL * rms[m])[0]
+        assert set(must.tolist()) <= chosen, f"{what}: row {m} missed a clear top-{K} row"
+
+
+CASES = [
+    # path,     V,    d,   k,  r,   g,  M,  K
+    ("gemv", 1000, 512, 16, 4, 128, 1, 16),
+    ("gemv", 3000, 1024, 33, 7, 128, 2, 5),
+    ("skinny", 2500, 512, 64, 16, 128, 1, 8),    # single launch (matrix cores)
+    ("skinny", 1025, 384, 33, 7, 96, 17, 16),    # one logit in the last slice
+    ("skinny", 17, 256, 16, 4, 64, 3, 16),       # V barely above K
+    ("lds", 1500, 512, 64, 16, 128, 130, 16),
+    ("lds", 5000, 256, 16, 4, 32, 129, 1),
+    ("skinny", 300000, 128, 1, 1, 32, 2, 16),   # merge over more keys than registers hold (LDS)
+    ("skinny", 400000, 128, 1, 1, 32, 1, 16),   # ... and than LDS holds (read each round)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "{}-V{}_d{}_k{}_r{}_g{}_M{}_K{}".format(*c))
+def test_topk_matches_oracle(case):
+    path, V, d, k, r, g, M, K = case
+    say(f"topk {case}")
+    f = random_small_head(V, d, k, r, g, M, seed=V + d + 5 * M, n_outliers=2, outlier_factor=20.0)
+    h = load(f)
+    v, i, y = gpu_topk(h, f["X"], K, path=path)
+    ref = oracle_forward.forward(f, f["X"])
+    assert_logits_close(y, ref, what=str(case))
+    check_exact(v, i, y, K, str(case))
+    check_oracle(i, ref, K, str(case))
+    h.close()
+
+
+def test_topk_ties_resolve_to_lower_indices():
+    # all-zero hidden states: every logit is 0 and the top K are rows 0 .. K-1
+    for path, M in [("gemv", 1), ("skinny", 5), ("lds", 130)]:
+        say(f"topk ties path={path}")
+        f = random_small_head(3000, 512, 32, 8, 128, M, seed=4)
+        f["X"][:] = 0
+        h = load(f)
+        v, i, y = gpu_topk(h, f["X"], 16, path=path)
+        assert np.array_equal(i, np.tile(np.arange(16), (M, 1))) and not v.any()
+        h.close()
+
+
+def test_topk_first_entry_is_the_argmax_and_bad_k_is_rejected():
+    import torch
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    from packed_quantized_lm_amd.binding import ArcheadError
+    f = random_small_head(1500, 512, 32, 8, 128, 40, seed=6)
+    h = load(f)
+    _, i, y = gpu_topk(h, f["X"], 1)
+    y2, a = h.forward(x_tensor_from_bits(f["X"]), want_logits=True, want_argmax=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(i[:, 0], a.cpu().numpy())
+    for K in (0, 17):
+        with pytest.raises(ArcheadError):
+            h.forward_topk(x_tensor_from_bits(f["X"]), K)
+    h.close()
+    small = random_small_head(5, 128, 1, 1, 32, 1, seed=7)
+    hs = load(small)
+    with pytest.raises(ArcheadError):
+        hs.forward_topk(x_tensor_from_bits(small["X"]), 6)  # K > V
+    v, i, y = gpu_topk(hs, small["X"], 5)
+    check_exact(v, i, y, 5, "V = K = 5")
+    hs.close()
+
+
+@pytest.mark.parametrize("name", ["qwen_m1", "qwen_m32", "large_m8", "qwen_m2048"])
+def test_topk_full_size(name):
+    say(f"topk full size {name}")
+    c = make_config(name)
+    h = load(c)
+    v, i, y = gpu_topk(h, c["X"], 16)
+    for m0 in range(0, c["M"], 256):
+        sl = slice(m0, m0 + 256)
+        check_exact(v[sl], i[sl], y[sl], 16, f"{name} rows {m0}..")
+    rows = np.arange(c["M"]) if c["M"] <= 32 else np.array([0, 1, c["M"] // 2, c["M"] - 1])
+    say(f"topk full size {name}: oracle for {rows.size} hidden states")
+    ref = oracle_forward.forward(c, c["X"][rows])
+    check_oracle(i[rows], ref, 16, name)
+    h.close()

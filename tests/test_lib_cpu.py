@@ -32,7 +32,8 @@ def test_header_declares_the_documented_entry_points():
     syms = declared_symbols()
     for name in ["archead_pack_load", "archead_forward", "archead_forward_argmax",
                  "archead_forward_path", "archead_forward_timed", "archead_forward_ce",
-                 "archead_forward_ce_path", "archead_reserve", "archead_packed_bytes",
+                 "archead_forward_ce_path", "archead_forward_topk", "archead_forward_topk_path",
+                 "archead_reserve", "archead_packed_bytes",
                  "archead_device_bytes", "archead_free", "archead_status_string",
                  "archead_last_error"]:
         assert name in syms
@@ -125,3 +126,11 @@ def test_forward_ce_rejects_missing_outputs_and_bad_handles(lib):
     assert lib.archead_forward_ce(None, 1, buf, None, None, None, buf, None, None) == binding.EINVAL
     assert lib.archead_forward_ce_path(ctypes.c_void_p(12345), 1, buf, None, None, None, buf, None, 0,
                                        None) == binding.EINVAL
+
+
+def test_forward_topk_rejects_missing_buffers_and_bad_handles(lib):
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call fails its checks first
+    assert lib.archead_forward_topk(None, 1, buf, 4, None, buf, buf, None) == binding.EINVAL
+    assert lib.archead_forward_topk(None, 1, buf, 4, buf, None, buf, None) == binding.EINVAL
+    assert lib.archead_forward_topk(None, 1, buf, 4, buf, buf, buf, None) == binding.EINVAL
+    assert "handle" in lib.archead_last_error().decode()
