@@ -85,7 +85,7 @@ def read_traffic(kernel_tag, workload):
     return data.get("hbm_bytes_per_launch")
 
 
-def measure(name, steps, warmup, copies, path="auto", with_logits=True):
+def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=True):
     import torch
     from packed_quantized_lm_amd import PackedHead, x_tensor_from_bits
     from packed_quantized_lm_amd.synth import make_config
@@ -151,8 +151,8 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True):
         del cg
     except Exception as e:  # report, do not hide: the direct-launch numbers stand
         log(f"{name}: graph capture failed: {e!r}")
-    ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path)
-    topk = measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits)
+    ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path) if extras else None
+    topk = measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits) if extras else None
     del heads
     torch.cuda.synchronize()
     # The events around the kernel add their own overhead to each launch.
@@ -334,6 +334,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the naive group-INT4 and SVD8+INT4 heads")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the forward step: no cross-entropy or top-k steps and no baseline "
+                         "heads (for profiles that must cover the forward's kernels alone)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many bytes "
                          "--steps times (calibration of the HBM byte counters)")
@@ -351,7 +354,8 @@ def main():
     from packed_quantized_lm_amd import load_library
     load_library()
 
-    head = measure(args.workload, args.steps, args.warmup, args.copies, path=args.path)
+    extras = not args.no_extras
+    head = measure(args.workload, args.steps, args.warmup, args.copies, path=args.path, extras=extras)
     log(json.dumps(head))
     secondary = []
     if not args.no_secondary:
@@ -359,7 +363,7 @@ def main():
                             ("large_m8", args.steps)]:
             if name == args.workload:
                 continue
-            s = measure(name, steps, max(2, args.warmup // 4), args.copies, path=args.path)
+            s = measure(name, steps, max(2, args.warmup // 4), args.copies, path=args.path, extras=extras)
             s["mfma_frac"] = s["path_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
             s["hbm_frac"] = s["vtile_GBs"] / HBM_PEAK_GBS
             log(json.dumps(s))
@@ -367,7 +371,7 @@ def main():
     # the baseline heads the pages compare against, on the same kernels and
     # the same rotated-copy timing, beside the packed head's step at that M
     baselines = []
-    if not args.no_baselines:
+    if not args.no_baselines and extras:
         same_m = {head["M"]: head["ms_per_step"]}
         same_m.update({s["M"]: s["ms_per_step"] for s in secondary if s["workload"].startswith("qwen")})
         for name, steps in [("int4_g32_m1", args.steps), ("svd8_int4_m1", args.steps),
@@ -409,8 +413,8 @@ def main():
                      "kernel_us": head["vtile_us_mean"],
                      "bytes_per_launch": head["vtile_bytes"]},
         "cpu_baseline": cpu,
-        "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]),
-        "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]),
+        "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
+        "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
         "secondary": secondary,
         "baselines": baselines,
     }
