@@ -84,10 +84,18 @@ __global__ __launch_bounds__(256) void topk_slice_kernel(TopkArgs a)
         return; // the whole wave
     const float *row = a.logits + m * a.V;
     uint64_t key[kTkPer];
+    // every load issued before any is used: the index is clamped rather than
+    // the load put under a branch (which would wait for each load in turn)
+    float y[kTkPer];
 #pragma unroll
     for (int c = 0; c < kTkPer; ++c) {
         const int64_t v = sl * kTkSlice + c * 64 + lane;
-        key[c] = v < a.V ? argmax_key(row[v], (uint32_t)v) : 0;
+        y[c] = row[v < a.V ? v : a.V - 1];
+    }
+#pragma unroll
+    for (int c = 0; c < kTkPer; ++c) {
+        const int64_t v = sl * kTkSlice + c * 64 + lane;
+        key[c] = v < a.V ? argmax_key(y[c], (uint32_t)v) : 0;
     }
     uint64_t mine = 0;
     for (int j = 0; j < a.K; ++j) {
@@ -127,10 +135,13 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a)
     if (n <= 256 * kTkReg) { // uniform: keys in registers, the winner dropped each round
         uint64_t key[kTkReg];
 #pragma unroll
-        for (int c = 0; c < kTkReg; ++c) {
+        for (int c = 0; c < kTkReg; ++c) { // clamped loads, all in flight at once
             const int64_t i = threadIdx.x + 256 * c;
-            key[c] = i < n ? src[i] : 0;
+            key[c] = src[i < n ? i : n - 1];
         }
+#pragma unroll
+        for (int c = 0; c < kTkReg; ++c)
+            key[c] = threadIdx.x + 256 * c < n ? key[c] : 0;
         for (int j = 0; j < a.K; ++j) {
             const uint64_t w = block_max(lane_max(key), j);
 #pragma unroll
