@@ -17,8 +17,9 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
 // a2-S: one streaming kernel over vocabulary tiles (any M; the packed codes
 // are streamed once per 32 hidden states): per v-block the low-rank codes,
 // then the SC4 residual, then the logits (if logits is not null) and, if
-// argmax is not null, the per-workgroup top-1 partials in w.part, which
-// launch_argmax reduces.
+// argmax is not null, the per-workgroup top-1 partials in w.part (and, with
+// w.want_lse, the log-sum-exp summaries in w.lsep), which launch_finish
+// reduces.
 hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
                                int32_t *argmax, hipStream_t st);
 
