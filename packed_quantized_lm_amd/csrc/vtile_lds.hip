@@ -20,13 +20,15 @@
 //      most 2^-12 of this, the smallest, term; q and the power-of-two rescale
 //      are exact), A = X 2^f_m in fp16 (exact for every element within 2^29
 //      of the row's largest operand);
-//   2. rescale the accumulator (fp32) to units of sC[v] 2^-f_m; correction:
-//      B = the exact integer codes C8, A = the fp16 hi + lo parts of
-//      s 2^f_m (22 significant bits);
-//   3. rescale to units of sA[v] 2^-f_m; core: B = the exact integer codes
-//      A5, A = hi + lo of t 2^f_m;
-// and the epilogue multiplies by sA[v] 2^-f_m.  Rows whose sC (sA) is zero
-// have their C8 (A5) codes masked and keep a unit divisor.
+//   2. rescale the accumulator (fp32) to units of sA[v] 2^-f_m; core:
+//      B = the exact integer codes A5, A = the fp16 hi + lo parts of
+//      t 2^f_m (22 significant bits);
+//   3. rescale to units of sC[v] 2^-f_m; correction: B = the exact integer
+//      codes C8, A = hi + lo of s 2^f_m;
+// and the epilogue multiplies by sC[v] 2^-f_m.  Rows whose sA (sC) is zero
+// have their A5 (C8) codes masked and keep a unit divisor.  The correction
+// phase goes last because its stage count (one stage per two K-steps of s)
+// is often odd: the last phase needs no pad stage.
 //
 // Tiles are assigned to the XCDs (workgroup b runs on XCD b mod 8) so that
 // operands are shared in an XCD's L2.  When the m-tile count is a multiple
@@ -63,9 +65,11 @@ constexpr int kLStageWords = kLScOff + 4 * kLVR * 8; // residual scales [4 K-ste
 // zeros.
 // ---------------------------------------------------------------------------
 // Stages of the tile kernel, in order: nsr residual stages (one K-chunk
-// each), nsc correction stages, nsa core stages; each count padded to even.
+// each), nsa core stages, nsc correction stages.  The residual and core
+// counts are padded to even (a stage pair shares the two LDS buffers); the
+// correction phase comes last and is not padded.
 struct LdsStages {
-    int nst, p1, p2; // stage count; the correction and core phases start at p1, p2
+    int nst, p1, p2; // stage count; the core and correction phases start at p1, p2
     int nkc, nc, na, kst, rst, gsteps, nks;
 };
 
@@ -79,10 +83,10 @@ static LdsStages lds_stage_info(const Shape &s)
     t.rst = (int)s.rst();
     t.gsteps = (int)(s.g / kKStep);
     t.nks = (int)(s.d / kKStep);
-    const int nsr = (t.nkc + 1) / 2 * 2, nsc = (t.nc + 1) / 2 * 2, nsa = ((t.kst + 1) / 2 + 1) / 2 * 2;
+    const int nsr = (t.nkc + 1) / 2 * 2, nsa = ((t.kst + 1) / 2 + 1) / 2 * 2, nsc = t.nc;
     t.p1 = nsr;
-    t.p2 = nsr + nsc;
-    t.nst = nsr + nsc + nsa;
+    t.p2 = nsr + nsa;
+    t.nst = nsr + nsa + nsc;
     return t;
 }
 
@@ -94,9 +98,10 @@ static LdsStages lds_stage_info(const Shape &s)
 // The tile adds its own m-block and v-block offsets.
 __device__ void lds_fill_entry(int s, const LdsStages &t, int32_t *e)
 {
-    const bool isr = s < t.p1, isc = !isr && s < t.p2;
+    const bool isr = s < t.p1, isc = s >= t.p2; // else core
     const int kc = s < t.nkc ? s : t.nkc - 1;
-    const int j1 = s - t.p1 > 0 ? s - t.p1 : 0, j2 = s - t.p2 > 0 ? s - t.p2 : 0;
+    // stage index within the correction (j1) and core (j2) phases
+    const int j1 = s - t.p2 > 0 ? s - t.p2 : 0, j2 = s - t.p1 > 0 ? s - t.p1 : 0;
     const int rl = t.rst > 0 ? t.rst - 1 : 0, kl = t.kst > 0 ? t.kst - 1 : 0;
     e[0] = isr ? 0 : isc ? 1 : 2;
     e[1] = isr ? t.nks : isc ? 2 * t.rst : 2 * t.kst;
@@ -289,7 +294,7 @@ struct LdsArgs {
     int want_argmax;
     int gsteps;
     int64_t nvb, nkc, G, na, nc, kst, rst;
-    int64_t nsr, nsc, nsa; // residual / correction / core stages, each padded to even
+    int64_t nsr, nsc, nsa; // residual / correction / core stages (residual and core padded to even)
     int64_t n_vr, n_mt, n_tiles, per_xcd;
     int mt_major; // XCD x owns m-tiles x, x + 8, ... (n_mt % 8 == 0)
 };
@@ -304,14 +309,14 @@ __device__ __forceinline__ void lds_dma4(const void *src, uint32_t *dst)
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
 }
 
-// Stages, in order: nsc correction stages (K-steps 2j, 2j+1 of s), nsa core
-// stages (K-steps 2j, 2j+1 of t), nkc residual stages (the four K-steps of
-// K-chunk kc of X), then one pad stage when the count is odd.  Each stage
-// has four operand slots q, each with 8 A blocks (one per m-block) and one B
-// operand per v-block: correction and core slot q = 2 hh + half takes the hi
-// or lo part of K-step 2j + hh; residual slot q is K-step q.  Every stage
-// runs the same 128 MFMAs per wave; slots past the end of a phase, and the
-// pad stage, have their B operands masked to zero.
+// Stages, in order: nsr residual stages (the four K-steps of K-chunk kc of
+// X; a pad stage when nkc is odd), nsa core stages (K-steps 2j, 2j+1 of t;
+// padded to even) and nc correction stages (K-steps 2j, 2j+1 of s).  Each
+// stage has four operand slots q, each with 8 A blocks (one per m-block)
+// and one B operand per v-block: core and correction slot q = 2 hh + half
+// takes the hi or lo part of K-step 2j + hh; residual slot q is K-step q.
+// Every stage runs the same 128 MFMAs per wave; slots past the end of a
+// phase, and pad stages, have their B operands masked to zero.
 template <int GS>
 __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 {
@@ -342,8 +347,8 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
     }
     const int64_t M = a.w.M, d = a.h.s.d, V = a.h.s.V;
     const int64_t nvb = a.nvb, G = a.G, nkc = a.nkc, kst = a.kst, rst = a.rst;
-    // stage ranges: residual [0, p1), correction [p1, p2), core [p2, nst)
-    const int64_t p1 = a.nsr, p2 = a.nsr + a.nsc, nst = a.nsr + a.nsc + a.nsa;
+    // stage ranges: residual [0, p1), core [p1, p2), correction [p2, nst)
+    const int64_t p1 = a.nsr, p2 = a.nsr + a.nsa, nst = a.nsr + a.nsa + a.nsc;
     const int64_t mbase = mt * kLRows, mb16_0 = mt * kLMB;
     const int64_t wg_vb0 = vr * kLVR;
     const int64_t vb0 = wg_vb0 + wv * kLVB;
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 #pragma unroll
         for (int i = 0; i < kLS; ++i)
             lds_dma16(abase + (fmb0 + i) * mstride + lane16, buf + (wv * kLS + i) * 256);
-        if (s < p2) { // one whole chunk per v-block: [lane][4 words], 16-byte copies
+        if (s < p1 || s >= p2) { // residual, correction: one whole chunk per v-block, 16-byte copies
 #pragma unroll
             for (int v = 0; v < kLVB; ++v)
                 lds_dma16(c0 + vb[v] * 1024 + lane16, buf + kLCodeOff + (wv * kLVB + v) * 256);
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         }
     };
     auto compute_c8 = [&](int64_t s, const uint32_t *buf) __attribute__((always_inline)) {
-        const int64_t j = s - p1;
+        const int64_t j = s - p2;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const uint32_t live = (j < a.nc && 2 * j + hh < rst) ? 0xFFFFFFFFu : 0u;
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
         }
     };
     auto compute_a5 = [&](int64_t s, const uint32_t *buf) __attribute__((always_inline)) {
-        const int64_t j = s - p2;
+        const int64_t j = s - p1;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int64_t ks = 2 * j + hh;
@@ -507,9 +512,11 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 
     // Stage s (even) computes from s_buf0 while stage s+1 fills s_buf1; the
     // barrier after it also waits for that fill.  No fill is left in flight
-    // past the last stage.  Every phase has an even stage count.
+    // past the last stage.  Every phase starts on an even stage; only the
+    // last one may end on an odd count, whose final stage (in s_buf0, filled
+    // by the pair before it) runs alone.
 #define ARCHEAD_LDS_PHASE(S0, S1, COMPUTE)                                          \
-    for (int64_t s = (S0); s < (S1); s += 2) {                                     \
+    for (int64_t s = (S0); s + 1 < (S1); s += 2) {                                 \
         stage_fill(s + 1, s_buf1);                                                 \
         COMPUTE(s, s_buf0);                                                        \
         __syncthreads();                                                           \
@@ -517,34 +524,38 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
             stage_fill(s + 2, s_buf0);                                             \
         COMPUTE(s + 1, s_buf1);                                                    \
         __syncthreads();                                                           \
+    }                                                                              \
+    if (((S1) - (S0)) & 1) {                                                       \
+        COMPUTE((S1) - 1, s_buf0);                                                 \
+        __syncthreads();                                                           \
     }
 
     // phase 1: residual, in units of sR 2^(e_r - 10) 2^-f_m
     ARCHEAD_LDS_PHASE(0, p1, compute_r4)
-    // to units of sC 2^-f_m
-#pragma unroll
-    for (int v = 0; v < kLVB; ++v) {
-        const float f = a.h.rsc[vb[v] * kVB + lr] / pc(v);
-#pragma unroll
-        for (int mb = 0; mb < kLMB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                T[mb][v][i] *= f;
-    }
-    // phase 2: correction
-    ARCHEAD_LDS_PHASE(p1, p2, compute_c8)
     // to units of sA 2^-f_m
 #pragma unroll
     for (int v = 0; v < kLVB; ++v) {
-        const float f = pc(v) / pa(v);
+        const float f = a.h.rsc[vb[v] * kVB + lr] / pa(v);
 #pragma unroll
         for (int mb = 0; mb < kLMB; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 T[mb][v][i] *= f;
     }
-    // phase 3: core
-    ARCHEAD_LDS_PHASE(p2, nst, compute_a5)
+    // phase 2: core
+    ARCHEAD_LDS_PHASE(p1, p2, compute_a5)
+    // to units of sC 2^-f_m
+#pragma unroll
+    for (int v = 0; v < kLVB; ++v) {
+        const float f = pa(v) / pc(v);
+#pragma unroll
+        for (int mb = 0; mb < kLMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                T[mb][v][i] *= f;
+    }
+    // phase 3: correction (the only phase that may end on an odd stage)
+    ARCHEAD_LDS_PHASE(p2, nst, compute_c8)
 #undef ARCHEAD_LDS_PHASE
 
     // back to logits units; write logits, the workgroup's top-1 keys and
@@ -564,7 +575,7 @@ __global__ __launch_bounds__(kLW * 64, 1) void vtile_lds_kernel(LdsArgs a)
 #pragma unroll
             for (int v = 0; v < kLVB; ++v) {
                 const int64_t row = (vb0 + v) * kVB + lr;
-                y[v] = T[mb][v][i] * pa(v) * fi[i];
+                y[v] = T[mb][v][i] * pc(v) * fi[i];
                 if (m < M && vb0 + v < nvb && row < V) {
                     if (a.logits)
                         a.logits[m * V + row] = y[v];
@@ -677,8 +688,8 @@ hipError_t launch_vtile_lds(const DevHead &h, const Work &w, float *logits, int3
     a.rst = h.s.rst();
     const LdsStages t = lds_stage_info(h.s);
     a.nsr = t.p1;                  // one K-chunk per stage
-    a.nsc = t.p2 - t.p1;           // two correction K-steps per stage
-    a.nsa = t.nst - t.p2;          // two core K-steps per stage
+    a.nsa = t.p2 - t.p1;           // two core K-steps per stage
+    a.nsc = t.nst - t.p2;          // two correction K-steps per stage
     a.n_vr = a.w.n_part;
     a.n_mt = (w.M + kLRows - 1) / kLRows;
     a.n_tiles = a.n_vr * a.n_mt;
