@@ -23,7 +23,8 @@ packer   tiny-head construction (eqs 2-5): damped metric, core, SC4 residual,
          activation-metric correction, INT8 factors
 naive    ctypes loader for naive.c, an independent triple-loop forward in C
 select   top-k of the logits: larger value first, equal values by lower
-         index (the argmax's tie rule widened to K candidates)
+         index (the argmax's tie rule widened to K candidates); top-k
+         sampling at a temperature from a given uniform number
 softmax  log-normaliser lse = log sum_v exp(logits) and cross-entropy
          lse - logit[target] of the logits (abstract and section 1: the
          logits feed the softmax; the head is judged by cross-entropy and
@@ -38,7 +39,8 @@ Parity pins (what each function is checked against, in tests/):
              cases reducing to plain integer matrix products, a hand-worked
              example in tests/golden/forward_example.txt
   select  -- K = 1 against the pinned first-index argmax, Python-sort brute
-             force on small rows with many ties, hand-built ties with +-0
+             force on small rows with many ties, hand-built ties with +-0;
+             sampling: K = 1, equal values, the two-way closed form, tau -> 0
   softmax -- closed forms (equal logits: ln V; V = 1; two-way softplus),
              shift invariance, softmax sums to one, math.fsum brute force on
              tiny rows, scipy's logsumexp at overflow-prone magnitudes

@@ -8,6 +8,13 @@ first, equal values by lower index (the tie rule of the argmax, where -0 and
 +0 are equal).  Pins in tests/test_oracle_select.py: K = 1 against the
 oracle's pinned first-index argmax, brute force with Python's sort on small
 rows, and hand-built ties.
+
+Top-k sampling with temperature tau draws candidate j of the K with
+probability proportional to exp((values[j] - values[0]) / tau) (the softmax
+of the K logits at temperature tau; subtracting the largest changes nothing).
+The uniform number u in [0, 1) is an input: the draw is the first j whose
+cumulative weight exceeds u times the total.  Pins: K = 1, equal values
+(j = floor(u K)), the two-way closed form, u = 0, and tau -> 0 (greedy).
 """
 from __future__ import annotations
 
@@ -22,3 +29,17 @@ def top_k(logits: np.ndarray, K: int) -> tuple[np.ndarray, np.ndarray]:
     # a stable sort of the negated values keeps lower indices first among equals
     idx = np.argsort(-y, axis=1, kind="stable")[:, :K]
     return np.take_along_axis(y, idx, axis=1), idx
+
+
+def sample_top_k(values: np.ndarray, indices: np.ndarray, temperature: float,
+                 u: np.ndarray) -> np.ndarray:
+    """The vocabulary index drawn for each row from its top-k candidates."""
+    v = np.asarray(values, dtype=np.float64)
+    if temperature <= 0:
+        raise ValueError("temperature must be positive")
+    w = np.exp((v - v[:, :1]) / temperature)
+    c = np.cumsum(w, axis=1)
+    t = np.asarray(u, dtype=np.float64) * c[:, -1]
+    j = np.array([np.searchsorted(c[m], t[m], side="right") for m in range(v.shape[0])])
+    j = np.minimum(j, v.shape[1] - 1)
+    return np.asarray(indices)[np.arange(v.shape[0]), j]

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle.forward import argmax_first
-from oracle.select import top_k
+from oracle.select import sample_top_k, top_k
 
 
 def test_k1_is_the_first_argmax():
@@ -39,3 +39,24 @@ def test_rejects_bad_k():
         top_k(np.zeros((2, 5)), 6)
     with pytest.raises(ValueError):
         top_k(np.zeros((2, 5)), 0)
+
+
+def test_sampling_closed_forms():
+    idx = np.tile(np.arange(100, 116), (5, 1))
+    u = np.array([0.0, 0.1, 0.5, 0.93, 0.999])
+    # K = 1: always the only candidate
+    assert np.array_equal(sample_top_k(np.zeros((5, 1)), idx[:, :1], 0.7, u), np.full(5, 100))
+    # equal values: uniform over the K, j = floor(u K)
+    got = sample_top_k(np.full((5, 16), 2.5), idx, 1.3, u)
+    assert np.array_equal(got, 100 + np.floor(u * 16).astype(int))
+    # two candidates a > b: the second is drawn iff u >= 1 / (1 + exp((b - a) / tau))
+    a, b, tau = 1.0, 0.2, 0.5
+    p0 = 1 / (1 + np.exp((b - a) / tau))
+    uu = np.array([p0 - 1e-9, p0 + 1e-9, 0.0, 0.999])
+    got = sample_top_k(np.tile([a, b], (4, 1)), np.tile([7, 9], (4, 1)), tau, uu)
+    assert list(got) == [7, 9, 7, 9]
+    # tau -> 0: greedy (the largest) for every u < 1
+    v = np.tile(np.linspace(3, 0, 16), (5, 1))
+    assert np.array_equal(sample_top_k(v, idx, 1e-3, u), np.full(5, 100))
+    with pytest.raises(ValueError):
+        sample_top_k(v, idx, 0.0, u)
