@@ -234,6 +234,23 @@ archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, 
                                          float *values, int32_t *indices, int path, void *hip_stream);
 
 /*
+ * archead_forward_sample -- archead_forward_topk plus one draw per hidden
+ * state from its K candidates at temperature tau (top-k sampling): candidate
+ * j weighs exp((values[m, j] - values[m, 0]) / tau), and the draw is the
+ * first j whose running sum of weights exceeds u[m] times their total;
+ * samples[m] = indices[m, j].  The weights and sums are fp32.
+ *
+ * temperature  tau > 0 and finite, else ARCHEAD_EINVAL.
+ * u            DEVICE fp32 M, uniform numbers in [0, 1) drawn by the caller
+ *              (a value outside [0, 1) picks the first or the last candidate).
+ * samples      DEVICE int32 M.
+ * K, logits, values, indices as archead_forward_topk (all required).
+ */
+archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int32_t K, float temperature,
+                                      const float *u, float *logits, float *values, int32_t *indices,
+                                      int32_t *samples, void *hip_stream);
+
+/*
  * archead_packed_bytes -- eq 10 of the ARCHead paper: the sum over the
  * registered packed buffers of numel x element size (A5 counted at 5 bits,
  * R4 at 4 bits, int8 fields at 8, scales at 16; each buffer rounded up to a

@@ -34,6 +34,8 @@ SIGNATURES = {
     "archead_forward_topk": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
     "archead_forward_topk_path": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int,
                                                  _VP]),
+    "archead_forward_sample": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, ctypes.c_float, _VP, _VP, _VP, _VP,
+                                              _VP, _VP]),
     "archead_forward_ce_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int, _VP]),
     "archead_packed_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
@@ -207,6 +209,28 @@ class PackedHead:
         indices = torch.empty((M, K), dtype=torch.int32, device=X.device)
         self.forward_topk_into(X, K, logits, values, indices, path=path, stream=stream)
         return values, indices, logits
+
+    def forward_sample_into(self, X, K: int, temperature: float, u, logits, values, indices, samples,
+                            stream=None):
+        """Enqueue the forward, the top K and one draw per row at the given
+        temperature from the uniform numbers u (fp32 M, in [0, 1))."""
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = load_library().archead_forward_sample(
+            self.handle, int(X.shape[0]), ptr(X), int(K), float(temperature), ptr(u), ptr(logits),
+            ptr(values), ptr(indices), ptr(samples), _stream_handle(stream))
+        _check(st, "archead_forward_sample")
+
+    def forward_sample(self, X, K: int, temperature: float, u, stream=None):
+        """Returns (samples int32 M, values M x K, indices M x K, logits M x V)."""
+        import torch
+        M = X.shape[0]
+        dev = X.device
+        logits = torch.empty((M, self.V), dtype=torch.float32, device=dev)
+        values = torch.empty((M, K), dtype=torch.float32, device=dev)
+        indices = torch.empty((M, K), dtype=torch.int32, device=dev)
+        samples = torch.empty((M,), dtype=torch.int32, device=dev)
+        self.forward_sample_into(X, K, temperature, u, logits, values, indices, samples, stream=stream)
+        return samples, values, indices, logits
 
     def forward(self, X, want_logits: bool = True, want_argmax: bool = False,
                 path: str | int = "auto", stream=None):

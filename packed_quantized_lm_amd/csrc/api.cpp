@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <set>
@@ -488,6 +489,23 @@ archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, 
         return st;
     Work w = make_work(h, M);
     HIP_TRY(launch_topk(w, logits, h->s.V, K, values, indices, (hipStream_t)hip_stream));
+    return ARCHEAD_OK;
+}
+
+archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int32_t K, float temperature,
+                                      const float *u, float *logits, float *values, int32_t *indices,
+                                      int32_t *samples, void *hip_stream)
+{
+    g_err.clear();
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(ARCHEAD_EINVAL, "temperature must be positive and finite");
+    if (!u || !samples)
+        return fail(ARCHEAD_EINVAL, "u and samples are required");
+    archead_status st =
+        archead_forward_topk_path(h, M, X, K, logits, values, indices, ARCHEAD_PATH_AUTO, hip_stream);
+    if (st != ARCHEAD_OK || M == 0)
+        return st;
+    HIP_TRY(launch_topk_sample(values, indices, M, K, temperature, u, samples, (hipStream_t)hip_stream));
     return ARCHEAD_OK;
 }
 

@@ -70,4 +70,9 @@ int64_t topk_slices(int64_t V);
 hipError_t launch_topk(const Work &w, const float *logits, int64_t V, int K, float *values,
                        int32_t *indices, hipStream_t st);
 
+// top-k sampling: per row, the index drawn from its K candidates (values in
+// descending order) at temperature > 0 with the uniform number u[m] in [0, 1).
+hipError_t launch_topk_sample(const float *values, const int32_t *indices, int64_t M, int K, float temperature,
+                              const float *u, int32_t *samples, hipStream_t st);
+
 } // namespace archead

@@ -181,6 +181,44 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(TopkArgs a)
     }
 }
 
+// Top-k sampling, one thread per row: candidate j weighs
+// exp((values[j] - values[0]) / tau) (computed as 2^(x log2 e / tau), x <= 0),
+// and the draw is the first j whose running sum exceeds u times the total.
+__global__ __launch_bounds__(256) void topk_sample_kernel(const float *values, const int32_t *indices, int64_t M,
+                                                          int K, float scale, const float *u, int32_t *out)
+{
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= M)
+        return;
+    float v[kTopKMax];
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) // clamped loads, all in flight at once
+        v[j] = values[m * K + (j < K ? j : K - 1)];
+    float cum[kTopKMax], c = 0.f;
+#pragma unroll
+    for (int j = 0; j < kTopKMax; ++j) {
+        c += j < K ? __builtin_amdgcn_exp2f((v[j] - v[0]) * scale) : 0.f;
+        cum[j] = c;
+    }
+    const float t = u[m] * c;
+    int pick = K - 1;
+#pragma unroll
+    for (int j = kTopKMax - 1; j >= 0; --j)
+        pick = (j < K && cum[j] > t) ? j : pick;
+    out[m] = indices[m * K + pick];
+}
+
+hipError_t launch_topk_sample(const float *values, const int32_t *indices, int64_t M, int K, float temperature,
+                              const float *u, int32_t *samples, hipStream_t st)
+{
+    if (M == 0)
+        return hipSuccess;
+    const float scale = 1.44269504088896340736f / temperature;
+    hipLaunchKernelGGL(topk_sample_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, st, values, indices, M,
+                       K, scale, u, samples);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const Work &w, const float *logits, int64_t V, int K, float *values,
                        int32_t *indices, hipStream_t st)
 {

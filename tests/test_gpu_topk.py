@@ -131,3 +131,39 @@ def test_topk_full_size(name):
     ref = oracle_forward.forward(c, c["X"][rows])
     check_oracle(i[rows], ref, 16, name)
     h.close()
+
+
+@pytest.mark.parametrize("path_M", [("gemv", 1), ("skinny", 40), ("lds", 130)])
+@pytest.mark.parametrize("tau", [0.7, 5.0, 1e-4])
+def test_topk_sampling_matches_oracle(path_M, tau):
+    """archead_forward_sample against oracle/select.py's draw over the GPU's own
+    top-k (exact inputs): equal, except where u lands within float rounding of
+    a cumulative boundary (the kernel sums in fp32), where either neighbour is
+    accepted.  At tau -> 0 the draw is the argmax; u = 0 always gives it."""
+    import torch
+    from oracle.select import sample_top_k
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    _, M = path_M
+    K = 16
+    say(f"topk sampling M={M} tau={tau}")
+    f = random_small_head(3000, 512, 32, 8, 128, M, seed=21 + M)
+    h = load(f)
+    X = x_tensor_from_bits(f["X"])
+    u = np.random.default_rng(M).random(M, dtype=np.float32)
+    u[0] = 0.0
+    s, v, i, y = h.forward_sample(X, K, tau, torch.from_numpy(u).cuda())
+    torch.cuda.synchronize()
+    s, v, i = s.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy()
+    check_exact(v, i.astype(np.int64), y.cpu().numpy(), K, "sampling top-k")
+    ref = sample_top_k(v, i, tau, u)
+    w = np.exp((v.astype(np.float64) - v[:, :1]) / tau)
+    c = np.cumsum(w, axis=1)
+    t = u * c[:, -1]
+    for m in range(M):
+        if s[m] != ref[m]:
+            near = np.min(np.abs(c[m] - t[m])) <= 1e-5 * c[m, -1]
+            assert near, f"row {m}: drew {s[m]}, oracle {ref[m]}"
+    assert s[0] == i[0, 0]
+    if tau == 1e-4:
+        assert np.array_equal(s, i[:, 0])
+    h.close()

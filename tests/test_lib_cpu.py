@@ -33,6 +33,7 @@ def test_header_declares_the_documented_entry_points():
     for name in ["archead_pack_load", "archead_forward", "archead_forward_argmax",
                  "archead_forward_path", "archead_forward_timed", "archead_forward_ce",
                  "archead_forward_ce_path", "archead_forward_topk", "archead_forward_topk_path",
+                 "archead_forward_sample",
                  "archead_reserve", "archead_packed_bytes",
                  "archead_device_bytes", "archead_free", "archead_status_string",
                  "archead_last_error"]:
@@ -134,3 +135,11 @@ def test_forward_topk_rejects_missing_buffers_and_bad_handles(lib):
     assert lib.archead_forward_topk(None, 1, buf, 4, buf, None, buf, None) == binding.EINVAL
     assert lib.archead_forward_topk(None, 1, buf, 4, buf, buf, buf, None) == binding.EINVAL
     assert "handle" in lib.archead_last_error().decode()
+
+
+def test_forward_sample_rejects_bad_temperature_and_missing_buffers(lib):
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call fails its checks first
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.archead_forward_sample(None, 1, buf, 4, tau, buf, buf, buf, buf, buf, None) == binding.EINVAL
+    assert lib.archead_forward_sample(None, 1, buf, 4, 1.0, None, buf, buf, buf, buf, None) == binding.EINVAL
+    assert lib.archead_forward_sample(None, 1, buf, 4, 1.0, buf, buf, buf, buf, buf, None) == binding.EINVAL
