@@ -153,6 +153,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
         log(f"{name}: graph capture failed: {e!r}")
     ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path) if extras else None
     topk = measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits) if extras else None
+    sample = measure_sample(heads, X, V, M, steps, warmup, per_graph, logits) if extras else None
     del heads
     torch.cuda.synchronize()
     # The events around the kernel add their own overhead to each launch.
@@ -177,6 +178,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
         "path_TFLOPs": fl / (best_ms / 1e3 / steps) / 1e12, "steps": steps,
         "ce": ce,
         "topk": topk,
+        "sample": sample,
     }
 
 
@@ -192,6 +194,21 @@ def measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits, K=16):
     idx = torch.empty((M, K), dtype=torch.int32, device="cuda")
     step = lambda i: heads[i % copies].forward_topk_into(X, K, logits, vals, idx, path=path)
     return _time_step(step, steps, warmup, per_graph, M, {"K": K})
+
+
+def measure_sample(heads, X, V, M, steps, warmup, per_graph, logits, K=16, temperature=0.8):
+    """The top-k step plus one draw per row at a temperature (a sampling
+    decode step), with fixed caller-drawn uniform numbers."""
+    import torch
+    if logits is None:
+        logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    copies = len(heads)
+    u = torch.rand((M,), dtype=torch.float32, device="cuda")
+    vals = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    idx = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    samples = torch.empty((M,), dtype=torch.int32, device="cuda")
+    step = lambda i: heads[i % copies].forward_sample_into(X, K, temperature, u, logits, vals, idx, samples)
+    return _time_step(step, steps, warmup, per_graph, M, {"K": K, "temperature": temperature})
 
 
 def _time_step(step, steps, warmup, per_graph, M, extra):
@@ -415,6 +432,8 @@ def main():
         "cpu_baseline": cpu,
         "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
         "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
+        "sample": dict(head["sample"], vs_argmax_step=head["sample"]["ms_per_step"] / head["ms_per_step"])
+        if extras else None,
         "secondary": secondary,
         "baselines": baselines,
     }
