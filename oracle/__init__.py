@@ -44,7 +44,14 @@ Parity pins (what each function is checked against, in tests/):
   softmax -- closed forms (equal logits: ln V; V = 1; two-way softplus),
              shift invariance, softmax sums to one, math.fsum brute force on
              tiny rows, scipy's logsumexp at overflow-prone magnitudes
-  packer  -- Eckart-Young-Mirsky tail energy, brute force over random and
-             grid rank-r candidates, the eigenvector route, the p = 1/2
-             identity with eq 1, the isotropic (C = I) reduction
+  packer  -- correction: Eckart-Young-Mirsky tail energy, brute force over
+             random and grid rank-r candidates, the eigenvector route, the
+             p = 1/2 identity with eq 1, the isotropic (C = I) reduction;
+             core and SC4 residual, from W and the stored fields alone: the
+             best rank-k approximation and tail energy by the eigenvectors of
+             W^T W, sqrt(sigma_i) in each core column / row within the norm
+             of the half-steps, residual scales fp16(absmax / 7) and codes
+             within half a step of W minus the unquantised best rank-k
+             product; planted mistakes (wrong triplets, sigma on one side,
+             residual of the quantised core) each fail one of these
 """

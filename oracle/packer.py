@@ -64,6 +64,13 @@ def truncated_svd(M: np.ndarray, rank: int):
     return U[:, :rank], S[:rank], Vt[:rank], S
 
 
+def core_factors(W: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Rank-k core of W (text under eq 3): the truncated SVD U_k S_k V_k^T in
+    the Frobenius sense, split as A_c = U_k S_k^(1/2), B_c = S_k^(1/2) V_k^T."""
+    U, S, Vt, _ = truncated_svd(W, k)
+    return U * np.sqrt(S)[None, :], np.sqrt(S)[:, None] * Vt
+
+
 def correction(E: np.ndarray, T: np.ndarray, T_inv: np.ndarray, r: int) -> dict:
     """Eqs 4-5: A_w = U_r Sigma_r, B_w = V_r^T T_p^-1 from the SVD of E T_p."""
     E_t = E @ T
@@ -79,12 +86,9 @@ def pack(W: np.ndarray, H: np.ndarray, k: int, r: int, g: int,
     V, d = W.shape
     met = metric_transform(H, p, lam)
 
-    # rank-k core, sqrt of the singular values to each side
-    U, S, Vt, _ = truncated_svd(W, k)
-    A_c = U * np.sqrt(S)[None, :]
-    B_c = np.sqrt(S)[:, None] * Vt
+    A_c, B_c = core_factors(W, k)
 
-    # eq 3
+    # eq 3: SC4 quantises the residual of the unquantised core
     A5, sA = quantize_groups(A_c, 5, None)
     B8, sB = quantize_groups(B_c, 8, None)
     R4v, sR = quantize_groups(W - A_c @ B_c, 4, g)

@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 from oracle import packer
-from oracle.layout import f16_bits_to_f64
-from oracle.quant import dequantize_groups
+from oracle.layout import f16_bits_to_f64, unpack_r4
+from oracle.quant import dequantize_groups, quantize_groups
 from packed_quantized_lm_amd.synth import make_config
 
 
@@ -191,3 +191,125 @@ def test_tiny_pack_lowers_the_logit_error_of_eq1(tiny):
     err_core = packer.logit_error(c["H"], W - inter["W_d"])
     err_full = packer.logit_error(c["H"], W - W_hat)
     assert err_full < 0.9 * err_core
+
+
+# --- the core and the SC4 residual (eq 3 and the text under it) -------------------
+#
+# These pins look only at W and at the stored fields, never at the packer's
+# intermediates.  W's singular structure comes from a second route, the
+# eigendecomposition of W^T W, so that a mistake in the packer's SVD step
+# (wrong triplets, wrong split of the singular values) or in the residual it
+# quantises (the quantised instead of the unquantised core) shows up.
+
+def _best_rank_k(W, k):
+    """Eckart-Young on W by the eigenvectors of W^T W: the best rank-k
+    approximation W V_k V_k^T, its tail energy and the top singular values."""
+    lam, Vfull = np.linalg.eigh(W.T @ W)
+    order = np.argsort(lam)[::-1]
+    lam, Vfull = np.clip(lam[order], 0, None), Vfull[:, order]
+    Vk = Vfull[:, :k]
+    return W @ Vk @ Vk.T, float(lam[k:].sum()), np.sqrt(lam[:k])
+
+
+def _core_and_residual_pins(W, f):
+    """Every check on (W, stored fields) that eq 3 with the readings taken fixes:
+    (1) sA o A5 and sB o B8 carry sqrt(sigma_i) in each column / row, up to the
+        norm of their half-steps (the sqrt split);
+    (2) their product is the best rank-k approximation of W up to the bound the
+        half-steps give (the right singular triplets);
+    (3) every residual group scale is fp16(absmax/7) of the group of
+        W - W_k, W_k the unquantised best rank-k product, and every residual
+        code lies within half a step of it (the residual of the unquantised core).
+    Returns the list of failed checks (empty when all hold)."""
+    k, g = f["k"], f["g"]
+    failed = []
+    best, _, sv = _best_rank_k(W, k)
+    sA = f16_bits_to_f64(f["sA"])
+    sB = f16_bits_to_f64(f["sB"])
+    A = f["A5"].astype(np.float64) * sA[:, None]
+    B = f["B8"].astype(np.float64) * sB[:, None]
+    hA = np.sqrt(np.sum((sA / 2) ** 2))                  # ||A_hat[:, i] - A_c[:, i]|| <= hA
+    hB = sB / 2 * np.sqrt(W.shape[1])                    # ||B_hat[i, :] - B_c[i, :]|| <= hB[i]
+    slack = 1e-9 * np.sqrt(sv[0])
+    if not np.all(np.abs(np.linalg.norm(A, axis=0) - np.sqrt(sv)) <= hA + slack):
+        failed.append("left core columns carry sqrt(sigma)")
+    if not np.all(np.abs(np.linalg.norm(B, axis=1) - np.sqrt(sv)) <= hB + slack):
+        failed.append("right core rows carry sqrt(sigma)")
+    # ||A_hat B_hat - A_c B_c||_F <= ||dA||_F ||B_hat||_2 + ||A_c||_2 ||dB||_F
+    dA = hA * np.sqrt(k)
+    dB = np.sqrt(np.sum(hB ** 2))
+    bound = dA * np.linalg.norm(B, 2) + np.sqrt(sv[0]) * dB
+    if not np.linalg.norm(A @ B - best) <= bound * (1 + 1e-9) + 1e-9 * sv[0]:
+        failed.append("core product is the best rank-k approximation")
+    R_ref = W - best
+    V, d = W.shape
+    sR = f16_bits_to_f64(f["sR"])
+    absmax = np.abs(R_ref.reshape(V, d // g, g)).max(axis=2)
+    if not np.all(np.abs(sR - absmax / 7) <= 2.0 ** -11 * absmax / 7 + 1e-12 * sv[0]):
+        failed.append("residual scales are fp16(absmax / 7) of W - W_k")
+    q = unpack_r4(f["R4"], d).astype(np.float64)
+    dev = np.abs(q * np.repeat(sR, g, axis=1) - R_ref)
+    if not np.all(dev <= np.repeat(sR, g, axis=1) / 2 * (1 + 1e-9) + 1e-12 * sv[0]):
+        failed.append("residual codes within half a step of W - W_k")
+    return failed
+
+
+@pytest.mark.parametrize("shape", [(40, 24, 5), (33, 64, 1), (2048, 256, 16)])
+def test_core_attains_the_eckart_young_tail_of_W(shape):
+    V, d, k = shape
+    rng = np.random.default_rng(11 + V)
+    W = rng.standard_normal((V, k + 2)) @ rng.standard_normal((k + 2, d)) + 0.1 * rng.standard_normal((V, d))
+    A_c, B_c = packer.core_factors(W, k)
+    best, tail, sv = _best_rank_k(W, k)
+    assert abs(np.sum((W - A_c @ B_c) ** 2) - tail) <= 1e-9 * np.sum(W ** 2)
+    assert np.allclose(A_c @ B_c, best, atol=1e-9 * np.abs(W).max())
+    # the sqrt split: column i of A_c and row i of B_c both have norm sqrt(sigma_i),
+    # and they are orthogonal families
+    assert np.allclose(np.linalg.norm(A_c, axis=0), np.sqrt(sv), rtol=1e-9)
+    assert np.allclose(np.linalg.norm(B_c, axis=1), np.sqrt(sv), rtol=1e-9)
+    G = A_c.T @ A_c
+    assert np.allclose(G - np.diag(np.diag(G)), 0, atol=1e-9 * sv[0])
+
+
+def test_no_random_rank_k_candidate_beats_the_core():
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((30, 12))
+    k = 3
+    A_c, B_c = packer.core_factors(W, k)
+    opt = float(np.sum((W - A_c @ B_c) ** 2))
+    for _ in range(3000):
+        B = rng.standard_normal((k, 12))
+        A = W @ np.linalg.pinv(B)                       # optimal left factor for B
+        assert np.sum((W - A @ B) ** 2) >= opt * (1 - 1e-12)
+
+
+def test_tiny_pack_core_and_residual_against_W(tiny):
+    c, f, _ = tiny
+    assert _core_and_residual_pins(c["W"], f) == []
+
+
+def _mutant_cores():
+    def wrong_triplets(W, k):        # singular triplets 1..k instead of 0..k-1
+        U, S, Vt = np.linalg.svd(W, full_matrices=False)
+        return U[:, 1:k + 1] * np.sqrt(S[1:k + 1]), np.sqrt(S[1:k + 1])[:, None] * Vt[1:k + 1]
+
+    def all_sigma_left(W, k):        # A_c = U S, B_c = V^T
+        U, S, Vt = np.linalg.svd(W, full_matrices=False)
+        return U[:, :k] * S[:k], Vt[:k]
+
+    def quantised_core(W, k):        # residual of the quantised core (the Q8 reading broken)
+        U, S, Vt = np.linalg.svd(W, full_matrices=False)
+        A_c, B_c = U[:, :k] * np.sqrt(S[:k]), np.sqrt(S[:k])[:, None] * Vt[:k]
+        return (dequantize_groups(*quantize_groups(A_c, 5, None), None),
+                dequantize_groups(*quantize_groups(B_c, 8, None), None))
+
+    return {"wrong triplets": wrong_triplets, "sigma on one side": all_sigma_left,
+            "residual of the quantised core": quantised_core}
+
+
+@pytest.mark.parametrize("name", list(_mutant_cores()))
+def test_core_pins_catch_planted_mistake(name, monkeypatch):
+    c = make_config("tiny")
+    monkeypatch.setattr(packer, "core_factors", _mutant_cores()[name])
+    f, _ = packer.pack(c["W"], c["H"], c["k"], c["r"], c["g"], p=0.75, lam=1e-2)
+    assert _core_and_residual_pins(c["W"], f), f"no pin caught the planted mistake: {name}"
