@@ -92,7 +92,12 @@ typedef enum archead_path {
  * correction factors and shape metadata; the dense V x D head is not kept).
  *
  * V, d, k, r, g  shape (see above).  Supported: V >= 1, V < 2^31;
- *                d a multiple of 128 in [128, 2^20]; g a multiple of 32 dividing d;
+ *                d a multiple of 128 in [128, 2^20] (the kernels stream the
+ *                residual in 128-column K-chunks, one 16-byte load per lane,
+ *                and read X in the same chunks straight from the caller's
+ *                buffer, so a ragged last chunk would need a padded copy of
+ *                X on every call; hidden sizes of LLM heads are multiples of
+ *                128); g a multiple of 32 dividing d;
  *                0 <= k <= 4096, 0 <= r <= 4096 (k = 0 or r = 0 drop the
  *                core or the correction term; the corresponding pointers
  *                may then be NULL).  Otherwise ARCHEAD_ESHAPE.
@@ -118,8 +123,14 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
 /*
  * archead_reserve -- size the handle's device workspace for up to M_max
  * hidden states per call, so that later forward calls with M <= M_max never
- * allocate.  A forward call with a larger M grows the workspace itself
- * (hipMalloc; the old buffer is freed after the device has drained it).
+ * allocate.  The call waits until the new workspace is ready.
+ * A forward call with a larger M grows the workspace itself, in stream
+ * order and without waiting: the new buffer is allocated and zeroed on the
+ * call's stream (hipMallocAsync), and the old one is released on that
+ * stream behind the work already enqueued there (hipFreeAsync).  A forward
+ * call that would grow the workspace while its stream is being captured
+ * into a HIP graph fails with ARCHEAD_EINVAL before enqueuing anything:
+ * reserve before capturing.
  * M_max < 0 -> ARCHEAD_EINVAL; M_max > 2^20 -> ARCHEAD_ESHAPE.
  */
 archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream);
@@ -240,7 +251,8 @@ archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, 
  * first j whose running sum of weights exceeds u[m] times their total;
  * samples[m] = indices[m, j].  The weights and sums are fp32.
  *
- * temperature  tau > 0 and finite, else ARCHEAD_EINVAL.
+ * temperature  tau > 0 and finite, with log2(e) / tau finite in fp32 (so no
+ *              subnormal tau), else ARCHEAD_EINVAL.
  * u            DEVICE fp32 M, uniform numbers in [0, 1) drawn by the caller
  *              (a value outside [0, 1) picks the first or the last candidate).
  * samples      DEVICE int32 M.

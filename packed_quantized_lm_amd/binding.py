@@ -89,6 +89,23 @@ def _stream_handle(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _need(t, name, dtypes, shape, device):
+    """Raise before any launch unless t is a contiguous device tensor of one of
+    dtypes, of the given shape, on device (the library takes raw pointers: a
+    host tensor or a wrong element type would be read as garbage or fault)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must live on {device}, not {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 _FIELD_DTYPES = [("A5", np.int8), ("sA", np.uint16), ("B8", np.int8), ("sB", np.uint16),
                  ("R4", np.uint8), ("sR", np.uint16), ("C8", np.int8), ("sC", np.uint16),
                  ("D8", np.int8), ("sD", np.uint16)]
@@ -131,11 +148,30 @@ class PackedHead:
         _check(load_library().archead_device_bytes(self.handle, ctypes.byref(out)), "archead_device_bytes")
         return out.value
 
+    def _check_x(self, X):
+        """X: a contiguous bf16 (or 16-bit bit-pattern) M x d device tensor; returns M."""
+        import torch
+        if not isinstance(X, torch.Tensor) or X.dim() != 2:
+            raise ValueError(f"X must be an M x {self.d} tensor")
+        if X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("X must hold bf16 values")
+        _need(X, "X", (X.dtype,), (X.shape[0], self.d), X.device)
+        return int(X.shape[0])
+
+    def _check_out(self, X, logits=None, argmax=None):
+        import torch
+        M = self._check_x(X)
+        if logits is not None:
+            _need(logits, "logits", (torch.float32,), (M, self.V), X.device)
+        if argmax is not None:
+            _need(argmax, "argmax", (torch.int32,), (M,), X.device)
+        return M
+
     def forward_into(self, X, logits, argmax, path: str | int = "auto", stream=None):
         """Enqueue the forward writing into preallocated torch tensors (either
         of logits / argmax may be None).  X: bf16 (or int16 bit patterns) M x d."""
         p = PATHS[path] if isinstance(path, str) else int(path)
-        M = int(X.shape[0])
+        M = self._check_out(X, logits, argmax)
         st = load_library().archead_forward_path(
             self.handle, M, ctypes.c_void_p(X.data_ptr()),
             None if logits is None else ctypes.c_void_p(logits.data_ptr()),
@@ -148,8 +184,9 @@ class PackedHead:
         """forward_into that also records the torch.cuda.Event pair around the
         vocabulary-tile kernel on the same stream."""
         p = PATHS[path] if isinstance(path, str) else int(path)
+        M = self._check_out(X, logits, argmax)
         st = load_library().archead_forward_timed(
-            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()),
+            self.handle, M, ctypes.c_void_p(X.data_ptr()),
             None if logits is None else ctypes.c_void_p(logits.data_ptr()),
             None if argmax is None else ctypes.c_void_p(argmax.data_ptr()),
             p, _stream_handle(stream), ctypes.c_void_p(ev_before.cuda_event),
@@ -161,12 +198,18 @@ class PackedHead:
         """Enqueue the forward with the log-normaliser lse (and, with int32
         targets, the cross-entropy nll) into preallocated torch tensors;
         targets / nll, logits and argmax may be None."""
+        import torch
         p = PATHS[path] if isinstance(path, str) else int(path)
+        M = self._check_out(X, logits, argmax)
+        for t, name, dt in ((targets, "targets", torch.int32), (lse, "lse", torch.float32),
+                            (nll, "nll", torch.float32)):
+            if t is not None:
+                _need(t, name, (dt,), (M,), X.device)
 
         def ptr(t):
             return None if t is None else ctypes.c_void_p(t.data_ptr())
         st = load_library().archead_forward_ce_path(
-            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()), ptr(targets), ptr(logits),
+            self.handle, M, ctypes.c_void_p(X.data_ptr()), ptr(targets), ptr(logits),
             ptr(argmax), ptr(lse), ptr(nll), p, _stream_handle(stream))
         _check(st, "archead_forward_ce_path")
 
@@ -193,9 +236,15 @@ class PackedHead:
     def forward_topk_into(self, X, K: int, logits, values, indices, path: str | int = "auto", stream=None):
         """Enqueue the forward plus the K largest logits per row into preallocated
         torch tensors (logits M x V, values M x K fp32, indices M x K int32)."""
+        import torch
         p = PATHS[path] if isinstance(path, str) else int(path)
+        M = self._check_out(X, logits)
+        if logits is None:
+            raise ValueError("logits is required")
+        _need(values, "values", (torch.float32,), (M, int(K)), X.device)
+        _need(indices, "indices", (torch.int32,), (M, int(K)), X.device)
         st = load_library().archead_forward_topk_path(
-            self.handle, int(X.shape[0]), ctypes.c_void_p(X.data_ptr()), int(K),
+            self.handle, M, ctypes.c_void_p(X.data_ptr()), int(K),
             ctypes.c_void_p(logits.data_ptr()), ctypes.c_void_p(values.data_ptr()),
             ctypes.c_void_p(indices.data_ptr()), p, _stream_handle(stream))
         _check(st, "archead_forward_topk_path")
@@ -214,9 +263,17 @@ class PackedHead:
                             stream=None):
         """Enqueue the forward, the top K and one draw per row at the given
         temperature from the uniform numbers u (fp32 M, in [0, 1))."""
+        import torch
+        M = self._check_out(X, logits)
+        if logits is None:
+            raise ValueError("logits is required")
+        _need(values, "values", (torch.float32,), (M, int(K)), X.device)
+        _need(indices, "indices", (torch.int32,), (M, int(K)), X.device)
+        _need(u, "u", (torch.float32,), (M,), X.device)
+        _need(samples, "samples", (torch.int32,), (M,), X.device)
         ptr = lambda t: ctypes.c_void_p(t.data_ptr())
         st = load_library().archead_forward_sample(
-            self.handle, int(X.shape[0]), ptr(X), int(K), float(temperature), ptr(u), ptr(logits),
+            self.handle, M, ptr(X), int(K), float(temperature), ptr(u), ptr(logits),
             ptr(values), ptr(indices), ptr(samples), _stream_handle(stream))
         _check(st, "archead_forward_sample")
 

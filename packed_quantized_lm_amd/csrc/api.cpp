@@ -125,24 +125,34 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     return L;
 }
 
+// Grows the workspace in stream order: the new buffer is allocated and zeroed
+// on st, and the old one is released on st behind the work already enqueued
+// there (which may still be reading it).  Nothing waits for the device.  A
+// stream that is being captured into a graph cannot grow it (the allocation
+// and the zero fill would become graph nodes that outlive this call's
+// bookkeeping): that is an error telling the caller to reserve first.
 archead_status grow_workspace(archead_t h, int64_t M, hipStream_t st)
 {
     if (M <= h->ws_M && h->ws)
         return ARCHEAD_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(st, &cap));
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(ARCHEAD_EINVAL, "the workspace holds M <= " + std::to_string(h->ws_M) + " and M = " +
+                                        std::to_string(M) + " would grow it while the stream is "
+                                        "capturing: call archead_reserve before the capture");
     WsLayout L = ws_layout(h->s, M);
-    if (h->ws) {
-        HIP_TRY(hipDeviceSynchronize());
-        HIP_TRY(hipFree(h->ws));
-        h->ws = nullptr;
-        h->ws_bytes = 0;
-        h->ws_M = 0;
-    }
     void *p = nullptr;
-    hipError_t e = hipMalloc(&p, L.total);
+    hipError_t e = hipMallocAsync(&p, L.total, st);
     if (e != hipSuccess)
-        return fail(ARCHEAD_ENOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
-    HIP_TRY(hipMemsetAsync(p, 0, L.total, st));
-    HIP_TRY(hipStreamSynchronize(st));
+        return fail(ARCHEAD_ENOMEM, std::string("workspace hipMallocAsync: ") + hipGetErrorString(e));
+    e = hipMemsetAsync(p, 0, L.total, st);
+    if (e != hipSuccess) {
+        (void)hipFreeAsync(p, st);
+        return fail(ARCHEAD_EHIP, std::string("workspace zero fill: ") + hipGetErrorString(e));
+    }
+    if (h->ws)
+        HIP_TRY(hipFreeAsync(h->ws, st));
     h->ws = p;
     h->ws_bytes = L.total;
     h->ws_M = M;
@@ -319,6 +329,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     h->ws_M = 0;
     h->device = dev;
     st = grow_workspace(h, 1, stream);
+    if (st == ARCHEAD_OK && hipStreamSynchronize(stream) != hipSuccess)
+        st = fail(ARCHEAD_EHIP, "workspace set-up did not complete");
     if (st != ARCHEAD_OK) {
         (void)hipFree(block);
         delete h;
@@ -342,7 +354,13 @@ archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream)
     if (M_max > kMaxM)
         return fail(ARCHEAD_ESHAPE, "M_max above 2^20");
     HIP_TRY(hipSetDevice(h->device));
-    return grow_workspace(h, std::max<int64_t>(M_max, 1), (hipStream_t)hip_stream);
+    archead_status st = grow_workspace(h, std::max<int64_t>(M_max, 1), (hipStream_t)hip_stream);
+    if (st != ARCHEAD_OK)
+        return st;
+    // a reservation is made ahead of the hot path: wait for it, so that the
+    // workspace is ready for calls on any stream
+    HIP_TRY(hipStreamSynchronize((hipStream_t)hip_stream));
+    return ARCHEAD_OK;
 }
 
 static archead_status forward_impl(archead_t h, int64_t M, const void *X, float *logits,
@@ -497,8 +515,11 @@ archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int
                                       int32_t *samples, void *hip_stream)
 {
     g_err.clear();
-    if (!(temperature > 0.f) || !std::isfinite(temperature))
-        return fail(ARCHEAD_EINVAL, "temperature must be positive and finite");
+    // the weights are 2^((v_j - v_0) log2(e) / tau): the factor log2(e) / tau
+    // must be finite too, which rules out subnormal temperatures
+    if (!(temperature > 0.f) || !std::isfinite(temperature) ||
+        !std::isfinite(1.4426950408889634f / temperature))
+        return fail(ARCHEAD_EINVAL, "temperature must be positive and finite, with log2(e) / temperature finite");
     if (!u || !samples)
         return fail(ARCHEAD_EINVAL, "u and samples are required");
     archead_status st =

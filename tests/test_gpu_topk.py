@@ -133,17 +133,30 @@ def test_topk_full_size(name):
     h.close()
 
 
-@pytest.mark.parametrize("path_M", [("gemv", 1), ("skinny", 40), ("lds", 130)])
-@pytest.mark.parametrize("tau", [0.7, 5.0, 1e-4])
-def test_topk_sampling_matches_oracle(path_M, tau):
-    """archead_forward_sample against oracle/select.py's draw over the GPU's own
-    top-k (exact inputs): equal, except where u lands within float rounding of
-    a cumulative boundary (the kernel sums in fp32), where either neighbour is
-    accepted.  At tau -> 0 the draw is the argmax; u = 0 always gives it."""
-    import torch
+def check_draw(s, v, i, u, tau, what):
+    """The draw against oracle/select.py's over the GPU's own top-k (exact
+    inputs): equal, except where u lands within float rounding of a
+    cumulative boundary (the kernel sums in fp32)."""
     from oracle.select import sample_top_k
+    ref = sample_top_k(v, i, tau, u)
+    w = np.exp((v.astype(np.float64) - v[:, :1]) / tau)
+    c = np.cumsum(w, axis=1)
+    t = u * c[:, -1]
+    for m in range(s.shape[0]):
+        if s[m] != ref[m]:
+            near = np.min(np.abs(c[m] - t[m])) <= 1e-5 * c[m, -1]
+            assert near, f"{what}: row {m}: drew {s[m]}, oracle {ref[m]}"
+
+
+# forward_sample takes the automatic path: M = 1 runs the single launch, M = 40
+# the streaming kernel, M = 130 the large-M kernel
+@pytest.mark.parametrize("M", [1, 40, 130])
+@pytest.mark.parametrize("tau", [0.7, 5.0, 1e-4])
+def test_topk_sampling_matches_oracle(M, tau):
+    """archead_forward_sample against the oracle's draw; at tau -> 0 the draw
+    is the argmax; u = 0 always gives it."""
+    import torch
     from packed_quantized_lm_amd import x_tensor_from_bits
-    _, M = path_M
     K = 16
     say(f"topk sampling M={M} tau={tau}")
     f = random_small_head(3000, 512, 32, 8, 128, M, seed=21 + M)
@@ -155,15 +168,32 @@ def test_topk_sampling_matches_oracle(path_M, tau):
     torch.cuda.synchronize()
     s, v, i = s.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy()
     check_exact(v, i.astype(np.int64), y.cpu().numpy(), K, "sampling top-k")
-    ref = sample_top_k(v, i, tau, u)
-    w = np.exp((v.astype(np.float64) - v[:, :1]) / tau)
-    c = np.cumsum(w, axis=1)
-    t = u * c[:, -1]
-    for m in range(M):
-        if s[m] != ref[m]:
-            near = np.min(np.abs(c[m] - t[m])) <= 1e-5 * c[m, -1]
-            assert near, f"row {m}: drew {s[m]}, oracle {ref[m]}"
+    check_draw(s, v, i, u, tau, "sampling")
     assert s[0] == i[0, 0]
     if tau == 1e-4:
         assert np.array_equal(s, i[:, 0])
+    h.close()
+
+
+@pytest.mark.parametrize("name", ["qwen_m1", "large_m8"])
+def test_topk_sampling_full_size(name):
+    """The draw at full size: the GPU's top-16 exact on its own logits and
+    within tolerance of the oracle's, the draw equal to the oracle's draw over
+    that top-16 (boundary rounding aside), at two temperatures."""
+    import torch
+    from packed_quantized_lm_amd import x_tensor_from_bits
+    say(f"topk sampling full size {name}")
+    c = make_config(name)
+    h = load(c)
+    X = x_tensor_from_bits(c["X"])
+    M = c["M"]
+    ref = oracle_forward.forward(c, c["X"])
+    for tau in (1.0, 0.3):
+        u = np.random.default_rng(int(100 * tau) + M).random(M, dtype=np.float32)
+        s, v, i, y = h.forward_sample(X, 16, tau, torch.from_numpy(u).cuda())
+        torch.cuda.synchronize()
+        s, v, i, y = s.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy(), y.cpu().numpy()
+        check_exact(v, i.astype(np.int64), y, 16, f"{name} tau={tau}")
+        check_oracle(i.astype(np.int64), ref, 16, f"{name} tau={tau}")
+        check_draw(s, v, i, u, tau, f"{name} tau={tau}")
     h.close()
