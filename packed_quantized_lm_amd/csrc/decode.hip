@@ -72,44 +72,6 @@ __device__ __forceinline__ void store_device(uint16_t *p, uint16_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// s_waitcnt vmcnt(0): every vector memory access of the wave, stores and
-// atomics included, has completed
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// s_waitcnt operand for vmcnt(n) alone (n < 64; low four bits at 3:0, high
-// two at 15:14; expcnt and lgkmcnt at their no-wait maxima)
-constexpr unsigned waitcnt_vm(unsigned n) { return (n & 15u) | ((n >> 4) & 3u) << 14 | 0x7u << 4 | 0xFu << 8; }
-static_assert(waitcnt_vm(0) == 0x0F70u, "vmcnt(0)");
-
-// Direct copy of one 16-byte piece per lane from global memory (p, per
-// lane) to LDS (dst + 16 lane; dst the same in every lane), sc1 (device
-// scope) when DEVICE.  Written as inline assembly because its callers wait
-// for the copy themselves with a partial vmcnt: the compiler, which cannot
-// tell which LDS reads a copy may alias, would wait for every outstanding
-// load (vmcnt(0)) before the next LDS read or barrier.  Hidden from the
-// compiler's count of outstanding loads, the copy can only make its waits
-// stricter than needed, never too weak.  M0 (the LDS base of the copy) is
-// restored afterwards.
-template <bool DEVICE>
-__device__ __forceinline__ void lds_dma16(const void *p, void *dst)
-{
-    const uint32_t base =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
-    uint32_t m0;
-    if constexpr (DEVICE)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %1, off sc1\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-                     : "=&s"(m0)
-                     : "v"(p), "s"(base)
-                     : "memory");
-    else
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-                     : "=&s"(m0)
-                     : "v"(p), "s"(base)
-                     : "memory");
-}
-
 // Keeps one K-step's loads and arithmetic together: no memory access moves
 // across it in the optimiser (empty asm with a memory clobber) or in the
 // machine scheduler.
@@ -383,6 +345,92 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         load_chunk(p.h1, 2 * pi + 1);
     };
 
+    // Completion count, run by wave 0 of every workgroup once the workgroup
+    // is done: projection-only workgroups are counted too (with no keys or
+    // summaries of their own), so the last workgroup counted -- which
+    // resolves the argmax and the log-normaliser and bumps the call counter
+    // -- comes after every workgroup of the grid, and the bump after every
+    // workgroup's read of the counter at its start.
+    auto count_and_finish = [&](bool with_keys) __attribute__((always_inline)) {
+        const int nall = a.ntwg + a.nwg;
+        const int nslot = nall < kSyncGroups ? nall : kSyncGroups;
+        const int slot = (int)(blockIdx.x % nslot);
+        const uint32_t slot_size = (uint32_t)((nall - 1 - slot) / nslot + 1);
+        if (with_keys && a.argmax && lane < MF) {
+            const uint64_t kk = umax64(umax64(red[0][lane], red[1][lane]), umax64(red[2][lane], red[3][lane]));
+            __hip_atomic_fetch_max(a.w.keys + slot * 32 + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (with_keys && a.w.want_lse && lane < MF) {
+            const LsePart p = lse_merge(lse_merge(lred[0][lane], lred[1][lane]), lse_merge(lred[2][lane], lred[3][lane]));
+            __hip_atomic_store(a.w.lsep + (int64_t)lane * a.nwg + bid, lse_bits(p), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vm_all();
+        uint32_t prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(sync + sync_slot_done(slot), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
+            uint32_t prev2 = 0;
+            if (lane == 0) {
+                __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if ((uint32_t)__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
+                if (a.argmax) {
+                    // lane s * MF + m takes (and clears) key m of slot s
+                    const int s = lane / MF, m = lane % MF;
+                    uint64_t kk = 0;
+                    if (s < nslot)
+                        kk = __hip_atomic_exchange(a.w.keys + s * 32 + m, (uint64_t)0, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    #pragma unroll
+                    for (int off = MF; off < kSyncGroups * MF; off <<= 1)
+                        kk = umax64(kk, shfl_xor_u64(kk, off));
+                    if (lane < MF)
+                        a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+                }
+                if (a.w.want_lse) {
+                    // every workgroup's summary is final once every slot is counted
+    #pragma unroll
+                    for (int m = 0; m < MF; ++m) {
+                        // the first 64 kLseBatch summaries with all their loads in
+                        // flight at once (one round trip), any further ones after
+                        const uint64_t *src = a.w.lsep + (int64_t)m * a.nwg;
+                        uint64_t bits[kLseBatch];
+    #pragma unroll
+                        for (int j = 0; j < kLseBatch; ++j) {
+                            const int i = lane + 64 * j;
+                            bits[j] = i < a.nwg ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                : kLseEmpty;
+                        }
+                        LsePart p{-__builtin_inff(), 0.f};
+    #pragma unroll
+                        for (int j = 0; j < kLseBatch; ++j)
+                            p = lse_merge(p, lse_unbits(bits[j]));
+                        for (int i = lane + 64 * kLseBatch; i < a.nwg; i += 64)
+                            p = lse_merge(p, lse_unbits(__hip_atomic_load(src + i, __ATOMIC_RELAXED,
+                                                                          __HIP_MEMORY_SCOPE_AGENT)));
+                        p = lse_merge64(p);
+                        if (lane == 0) {
+                            const float L = p.mx + logf(p.s);
+                            a.lse[m] = L;
+                            if (a.nll) {
+                                const int32_t t = a.w.targets[m];
+                                a.nll[m] = (t >= 0 && (int64_t)t < V)
+                                               ? L - __hip_atomic_load(a.w.tl + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                               : __builtin_nanf("");
+                            }
+                        }
+                    }
+                }
+                if (lane == 0) {
+                    __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(sync + sync_epoch(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    };
+
     // Projection columns.  With projection-only workgroups, their wave pw
     // publishes columns pw, pw + 4 ntwg, ...; they start at once, stream
     // nothing and leave.  Without them, streaming wave gw publishes columns
@@ -471,6 +519,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 __hip_atomic_fetch_add(sync + sync_published(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        __syncthreads(); // every column of this workgroup is published
+        if (wv == 0)
+            count_and_finish(false);
         return;
     }
     const int64_t gw = bid * 4 + wv, nw = (int64_t)a.nwg * 4;
@@ -971,82 +1022,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // point; each is complete before the count that follows it, so a slot's
     // keys are final once its count is full, and every key is final once
     // every slot is counted.
-    const int nslot = a.nwg < kSyncGroups ? a.nwg : kSyncGroups;
-    const int slot = (int)(bid % nslot);
-    const uint32_t slot_size = (uint32_t)((a.nwg - 1 - slot) / nslot + 1);
-    if (a.argmax && lane < MF) {
-        const uint64_t kk = umax64(umax64(red[0][lane], red[1][lane]), umax64(red[2][lane], red[3][lane]));
-        __hip_atomic_fetch_max(a.w.keys + slot * 32 + lane, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (a.w.want_lse && lane < MF) {
-        const LsePart p = lse_merge(lse_merge(lred[0][lane], lred[1][lane]), lse_merge(lred[2][lane], lred[3][lane]));
-        __hip_atomic_store(a.w.lsep + (int64_t)lane * a.nwg + bid, lse_bits(p), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    wait_vm_all();
-    uint32_t prev = 0;
-    if (lane == 0)
-        prev = __hip_atomic_fetch_add(sync + sync_slot_done(slot), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) == slot_size - 1) {
-        uint32_t prev2 = 0;
-        if (lane == 0) {
-            __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
-            if (a.argmax) {
-                // lane s * MF + m takes (and clears) key m of slot s
-                const int s = lane / MF, m = lane % MF;
-                uint64_t kk = 0;
-                if (s < nslot)
-                    kk = __hip_atomic_exchange(a.w.keys + s * 32 + m, (uint64_t)0, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int off = MF; off < kSyncGroups * MF; off <<= 1)
-                    kk = umax64(kk, shfl_xor_u64(kk, off));
-                if (lane < MF)
-                    a.argmax[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-            }
-            if (a.w.want_lse) {
-                // every workgroup's summary is final once every slot is counted
-#pragma unroll
-                for (int m = 0; m < MF; ++m) {
-                    // the first 64 kLseBatch summaries with all their loads in
-                    // flight at once (one round trip), any further ones after
-                    const uint64_t *src = a.w.lsep + (int64_t)m * a.nwg;
-                    uint64_t bits[kLseBatch];
-#pragma unroll
-                    for (int j = 0; j < kLseBatch; ++j) {
-                        const int i = lane + 64 * j;
-                        bits[j] = i < a.nwg ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                            : kLseEmpty;
-                    }
-                    LsePart p{-__builtin_inff(), 0.f};
-#pragma unroll
-                    for (int j = 0; j < kLseBatch; ++j)
-                        p = lse_merge(p, lse_unbits(bits[j]));
-                    for (int i = lane + 64 * kLseBatch; i < a.nwg; i += 64)
-                        p = lse_merge(p, lse_unbits(__hip_atomic_load(src + i, __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT)));
-                    p = lse_merge64(p);
-                    if (lane == 0) {
-                        const float L = p.mx + logf(p.s);
-                        a.lse[m] = L;
-                        if (a.nll) {
-                            const int32_t t = a.w.targets[m];
-                            a.nll[m] = (t >= 0 && (int64_t)t < V)
-                                           ? L - __hip_atomic_load(a.w.tl + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                           : __builtin_nanf("");
-                        }
-                    }
-                }
-            }
-            if (lane == 0) {
-                __hip_atomic_store(sync + sync_top_done(), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(sync + sync_epoch(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
+    count_and_finish(true);
     store_logits();
 }
 

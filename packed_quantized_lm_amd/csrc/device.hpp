@@ -277,4 +277,56 @@ __device__ __forceinline__ LsePart lse_merge64(LsePart p)
     return p;
 }
 
+// s_waitcnt vmcnt(0): every vector memory access of the wave, stores and
+// atomics included, has completed
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt operand for vmcnt(n) alone (n < 64; low four bits at 3:0, high
+// two at 15:14; expcnt and lgkmcnt at their no-wait maxima)
+constexpr unsigned waitcnt_vm(unsigned n) { return (n & 15u) | ((n >> 4) & 3u) << 14 | 0x7u << 4 | 0xFu << 8; }
+static_assert(waitcnt_vm(0) == 0x0F70u, "vmcnt(0)");
+
+// Direct copy of one 16-byte piece per lane from global memory (p, per
+// lane) to LDS (dst + 16 lane; dst the same in every lane), sc1 (device
+// scope) when DEVICE.  Written as inline assembly because its callers wait
+// for the copy themselves with a partial vmcnt: the compiler, which cannot
+// tell which LDS reads a copy may alias, would wait for every outstanding
+// load (vmcnt(0)) before the next LDS read or barrier.  Hidden from the
+// compiler's count of outstanding loads, the copy can only make its waits
+// stricter than needed, never too weak.  M0 (the LDS base of the copy) is
+// restored afterwards.
+template <bool DEVICE>
+__device__ __forceinline__ void lds_dma16(const void *p, void *dst)
+{
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+    uint32_t m0;
+    if constexpr (DEVICE)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off sc1\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                     : "=&s"(m0)
+                     : "v"(p), "s"(base)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                     : "=&s"(m0)
+                     : "v"(p), "s"(base)
+                     : "memory");
+}
+
+
+// The same for one 4-byte piece per lane (LDS dst + 4 lane).
+__device__ __forceinline__ void lds_dma4(const void *p, void *dst)
+{
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+    uint32_t m0;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(m0)
+                 : "v"(p), "s"(base)
+                 : "memory");
+}
+
 } // namespace archead
