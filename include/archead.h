@@ -164,6 +164,28 @@ archead_status archead_forward_argmax(archead_t h, int64_t M, const void *X, flo
                                       int32_t *argmax, void *hip_stream);
 
 /*
+ * archead_forward_argmax_noalloc -- archead_forward_argmax for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It never allocates or frees
+ * anything: the kernels' workspace is a fixed device array of 8 MiB per GPU
+ * inside the library, kept until the process ends.  Its address is looked
+ * up once per device, on the first call there.
+ *
+ * Arguments, results, numerics and stream behaviour are those of
+ * archead_forward_argmax (automatic path); the results are identical.
+ * A call whose workspace would exceed 8 MiB -> ARCHEAD_ESHAPE (for the
+ * 151936 x 4096 head with k = 256, r = 64 that is every M below 128; the
+ * large-M path needs more).
+ * Every call on a GPU, from any handle, shares that GPU's array, which keeps
+ * the last call's contents: each call first clears (with a small kernel on
+ * hip_stream) what must start at zero.  Calls that overlap on one GPU
+ * (different streams with no ordering between them) race and give
+ * undefined results; order them on one stream or with events.
+ */
+archead_status archead_forward_argmax_noalloc(archead_t h, int64_t M, const void *X, float *logits,
+                                              int32_t *argmax, void *hip_stream);
+
+/*
  * archead_forward_path -- archead_forward_argmax with the vocabulary-tile
  * kernel family forced (archead_path).  logits and argmax may each be NULL
  * (not both).  An unknown path -> ARCHEAD_EINVAL.  Every path computes the

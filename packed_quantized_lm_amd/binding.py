@@ -29,6 +29,7 @@ SIGNATURES = {
     "archead_forward": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP]),
     "archead_forward_argmax": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP]),
     "archead_forward_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP]),
+    "archead_forward_argmax_noalloc": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP]),
     "archead_forward_timed": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP]),
     "archead_forward_ce": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "archead_forward_topk": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP]),
@@ -178,6 +179,19 @@ class PackedHead:
             None if argmax is None else ctypes.c_void_p(argmax.data_ptr()),
             p, _stream_handle(stream))
         _check(st, "archead_forward_path")
+
+    def forward_argmax_noalloc_into(self, X, logits, argmax, stream=None):
+        """Enqueue archead_forward_argmax_noalloc: the forward and its argmax
+        into preallocated tensors (logits may be None), on the library's fixed
+        per-GPU workspace -- nothing is allocated."""
+        M = self._check_out(X, logits, argmax)
+        if argmax is None:
+            raise ValueError("argmax is required")
+        st = load_library().archead_forward_argmax_noalloc(
+            self.handle, M, ctypes.c_void_p(X.data_ptr()),
+            None if logits is None else ctypes.c_void_p(logits.data_ptr()),
+            ctypes.c_void_p(argmax.data_ptr()), _stream_handle(stream))
+        _check(st, "archead_forward_argmax_noalloc")
 
     def forward_timed(self, X, logits, argmax, ev_before, ev_after, path: str | int = "auto",
                       stream=None):

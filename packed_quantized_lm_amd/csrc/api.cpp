@@ -159,13 +159,14 @@ archead_status grow_workspace(archead_t h, int64_t M, hipStream_t st)
     return ARCHEAD_OK;
 }
 
-Work make_work(archead_t h, int64_t M)
+// The per-call view of a workspace at base laid out for up to cap rows.
+Work make_work_in(const Shape &s, void *base, int64_t cap, int64_t M)
 {
-    WsLayout L = ws_layout(h->s, h->ws_M);
-    char *b = (char *)h->ws;
+    WsLayout L = ws_layout(s, cap);
+    char *b = (char *)base;
     Work w;
     w.M = M;
-    w.Mp = round_m(h->ws_M);
+    w.Mp = round_m(cap);
     w.t16 = (uint16_t *)(b + L.t16);
     w.s16 = (uint16_t *)(b + L.s16);
     w.xsneg = (float *)(b + L.xsneg);
@@ -176,14 +177,14 @@ Work make_work(archead_t h, int64_t M)
     w.ssw = (uint16_t *)(b + L.ssw);
     w.xsc = (float *)(b + L.xsc);
     w.lfill = (int32_t *)(b + L.lfill);
-    w.Mq = round_m128(std::max<int64_t>(h->ws_M, 1));
+    w.Mq = round_m128(std::max<int64_t>(cap, 1));
     w.part = (uint64_t *)(b + L.part);
     w.n_part = 0;
-    w.part_cap = std::max<int64_t>(h->ws_M, 1) * max_n_part(h->s);
+    w.part_cap = std::max<int64_t>(cap, 1) * max_n_part(s);
     w.lsep = (uint64_t *)(b + L.lsep);
     w.tl = (float *)(b + L.tl);
     w.tkp = (uint64_t *)(b + L.tkp);
-    w.tkp_cap = std::max<int64_t>(h->ws_M, 1) * topk_slices(h->s.V) * kTopKMax;
+    w.tkp_cap = std::max<int64_t>(cap, 1) * topk_slices(s.V) * kTopKMax;
     w.want_lse = 0;
     w.targets = nullptr;
     w.sync = (uint32_t *)(b + L.sync);
@@ -191,6 +192,8 @@ Work make_work(archead_t h, int64_t M)
     w.colflag = (uint32_t *)(b + L.colflag);
     return w;
 }
+
+Work make_work(archead_t h, int64_t M) { return make_work_in(h->s, h->ws, h->ws_M, M); }
 
 archead_status validate_shape(int64_t V, int64_t d, int64_t k, int64_t r, int64_t g)
 {
@@ -208,6 +211,29 @@ archead_status validate_shape(int64_t V, int64_t d, int64_t k, int64_t r, int64_
 }
 
 } // namespace
+
+namespace archead {
+
+archead_status api_fail(archead_status s, const std::string &msg) { return fail(s, msg); }
+
+archead_status handle_device(archead_t h, int *device)
+{
+    g_err.clear();
+    if (!live(h))
+        return fail(ARCHEAD_EINVAL, "invalid or freed handle");
+    *device = h->device;
+    return ARCHEAD_OK;
+}
+
+size_t workspace_bytes(archead_t h, int64_t M, size_t *zero_head, size_t *zero_tail)
+{
+    const WsLayout L = ws_layout(h->s, std::max<int64_t>(M, 1));
+    *zero_head = L.xsneg; // t16, s16: their padding columns must read as zero
+    *zero_tail = L.sync;  // sync, keys, colflag: counters that start at zero
+    return L.total;
+}
+
+} // namespace archead
 
 extern "C" {
 
@@ -363,10 +389,13 @@ archead_status archead_reserve(archead_t h, int64_t M_max, void *hip_stream)
     return ARCHEAD_OK;
 }
 
+// ws_ext: a caller-provided workspace laid out for ws_cap rows (nothing is
+// allocated then); otherwise the handle's own, grown as needed.
 static archead_status forward_impl(archead_t h, int64_t M, const void *X, float *logits,
                                    int32_t *argmax, int path, void *hip_stream, hipEvent_t ev0,
                                    hipEvent_t ev1, const int32_t *targets = nullptr,
-                                   float *lse = nullptr, float *nll = nullptr)
+                                   float *lse = nullptr, float *nll = nullptr, void *ws_ext = nullptr,
+                                   int64_t ws_cap = 0)
 {
     g_err.clear();
     if (!live(h))
@@ -391,9 +420,13 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
         return fail(ARCHEAD_EINVAL, "X must be 16-byte aligned");
     hipStream_t st = (hipStream_t)hip_stream;
     HIP_TRY(hipSetDevice(h->device));
-    archead_status s = grow_workspace(h, M, st);
-    if (s != ARCHEAD_OK)
-        return s;
+    if (!ws_ext) {
+        archead_status s = grow_workspace(h, M, st);
+        if (s != ARCHEAD_OK)
+            return s;
+    } else if (ws_cap < M) {
+        return fail(ARCHEAD_EINVAL, "workspace too small");
+    }
 
     int chosen = path;
     if (chosen == ARCHEAD_PATH_AUTO) {
@@ -410,7 +443,7 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     const bool one_launch = chosen == ARCHEAD_PATH_GEMV ||
                             (chosen == ARCHEAD_PATH_SKINNY && decode_ok(h->dev, M, true));
 
-    Work w = make_work(h, M);
+    Work w = ws_ext ? make_work_in(h->s, ws_ext, ws_cap, M) : make_work(h, M);
     w.want_lse = lse ? 1 : 0;
     w.targets = targets;
     const uint16_t *Xb = (const uint16_t *)X;
@@ -592,3 +625,14 @@ archead_status archead_free(archead_t h)
 }
 
 } // extern "C"
+
+namespace archead {
+
+archead_status forward_in_workspace(archead_t h, int64_t M, const void *X, float *logits, int32_t *argmax,
+                                    void *hip_stream, void *ws, int64_t ws_cap)
+{
+    return forward_impl(h, M, X, logits, argmax, ARCHEAD_PATH_AUTO, hip_stream, nullptr, nullptr, nullptr,
+                        nullptr, nullptr, ws, ws_cap);
+}
+
+} // namespace archead
