@@ -78,7 +78,7 @@ int64_t round_m128(int64_t M) { return (M + 127) / 128 * 128; }
 
 int64_t max_n_part(const Shape &s)
 {
-    return std::max<int64_t>(std::max(skinny_max_n_part(s), lds_max_n_part(s)), 1);
+    return std::max<int64_t>(std::max({skinny_max_n_part(s), lds_max_n_part(s), stream2_max_n_part(s)}), 1);
 }
 
 WsLayout ws_layout(const Shape &s, int64_t Mmax)
@@ -461,16 +461,22 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     } else {
         HIP_TRY(launch_proj(h->dev, w, Xb, st));
     }
+    // batched decode on the persistent slab-staged kernel where it applies
+    const bool s2 = chosen == ARCHEAD_PATH_SKINNY && stream2_ok(h->dev, M);
     if (ev0)
         HIP_TRY(hipEventRecord(ev0, st));
     if (chosen == ARCHEAD_PATH_LDS)
         HIP_TRY(launch_vtile_lds(h->dev, w, logits, argmax, st));
+    else if (s2)
+        HIP_TRY(launch_vtile_stream2(h->dev, w, Xb, logits, argmax, st));
     else
         HIP_TRY(launch_vtile_skinny(h->dev, w, Xb, logits, argmax, st));
     if (ev1)
         HIP_TRY(hipEventRecord(ev1, st));
     if (argmax || lse) {
-        const int64_t n_part = chosen == ARCHEAD_PATH_LDS ? lds_n_part(h->dev, M) : skinny_n_part(h->dev, M);
+        const int64_t n_part = chosen == ARCHEAD_PATH_LDS ? lds_n_part(h->dev, M)
+                               : s2                       ? stream2_n_part(h->dev, M)
+                                                          : skinny_n_part(h->dev, M);
         HIP_TRY(launch_finish(w, n_part, h->s.V, argmax, lse, nll, st));
     }
     return ARCHEAD_OK;

@@ -28,6 +28,16 @@ hipError_t launch_vtile_skinny(const DevHead &h, const Work &w, const uint16_t *
 int64_t skinny_n_part(const DevHead &h, int64_t M);
 int64_t skinny_max_n_part(const Shape &s);
 
+// a2-S for batched decode (2 <= M <= 32, g = 128): one persistent streaming
+// kernel, one workgroup of 8 waves per compute unit, X staged in LDS slab by
+// slab (vtile2.hip).  Needs launch_proj first; argmax partials as for the
+// other a2-S kernel, one per workgroup.
+bool stream2_ok(const DevHead &h, int64_t M);
+int64_t stream2_n_part(const DevHead &h, int64_t M);
+int64_t stream2_max_n_part(const Shape &s);
+hipError_t launch_vtile_stream2(const DevHead &h, const Work &w, const uint16_t *X, float *logits,
+                                int32_t *argmax, hipStream_t st);
+
 // a2-L: LDS-staged fp16 MFMA over [128 hidden states x 512 vocabulary rows]
 // tiles for large M.  Needs launch_proj_mfma then launch_prep_lds first.
 // Every B operand is an integer code times its row-normalised scale, rounded

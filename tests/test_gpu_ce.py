@@ -87,6 +87,8 @@ CASES = [
     ("skinny", 1000, 384, 33, 7, 96, 17),
     ("skinny", 4099, 640, 64, 48, 128, 33),
     ("skinny", 777, 512, 0, 16, 256, 8),      # no core term
+    ("skinny", 3001, 1024, 40, 20, 128, 9),   # persistent batched-decode kernel, one m-tile
+    ("skinny", 2050, 1536, 96, 33, 128, 32),  # the same, two m-tiles
     ("lds", 17, 256, 16, 4, 64, 3),
     ("lds", 1500, 512, 64, 16, 128, 130),     # several tiles, ragged tails in V and M
     ("lds", 600, 256, 16, 4, 32, 257),

@@ -86,6 +86,43 @@ def test_ragged_shapes(shape, path):
     h.close()
 
 
+# --- the persistent batched-decode kernel (2 <= M <= 32, g = 128, d a multiple of 512):
+# one and two m-tiles, ragged last v-blocks and wave ranges, missing terms ----------
+
+BATCHED_SHAPES = [
+    # V,     d,    k,   r,   g,  M
+    (1, 512, 1, 1, 128, 2),
+    (33, 512, 8, 4, 128, 3),
+    (4099, 512, 40, 20, 128, 7),
+    (2050, 1536, 96, 33, 128, 16),
+    (2050, 1536, 96, 33, 128, 17),
+    (9001, 1024, 64, 16, 128, 31),
+    (6000, 2560, 192, 48, 128, 32),
+    (777, 512, 0, 16, 128, 12),    # no core term
+    (777, 1024, 40, 0, 128, 20),   # no correction term
+    (500, 512, 0, 0, 128, 25),     # residual only
+    (40000, 512, 16, 8, 128, 9),   # several v-blocks per wave
+]
+
+
+@pytest.mark.parametrize("shape", BATCHED_SHAPES, ids=lambda s: "V{}_d{}_k{}_r{}_g{}_M{}".format(*s))
+def test_batched_decode_shapes(shape):
+    V, d, k, r, g, M = shape
+    say(f"batched decode {shape}")
+    f = random_small_head(V, d, k, r, g, M, seed=V * 11 + d + M, n_outliers=2, outlier_factor=20.0)
+    h = load(f)
+    ref = oracle_forward.forward(f, f["X"])
+    y, a = gpu_forward(h, f["X"], path="skinny")
+    assert_logits_close(y, ref, what=str(shape))
+    assert_argmax_ok(a, y, ref, what=str(shape))
+    # argmax alone and logits alone give the same results
+    _, a2 = gpu_forward(h, f["X"], path="skinny", want_logits=False)
+    y3, _ = gpu_forward(h, f["X"], path="skinny", want_argmax=False)
+    assert np.array_equal(a, a2)
+    assert np.array_equal(y, y3)
+    h.close()
+
+
 # --- several m-tiles and v-ranges of the large-M kernel, ragged in both -------------
 
 LDS_SHAPES = [
