@@ -151,6 +151,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
         del cg
     except Exception as e:  # report, do not hide: the direct-launch numbers stand
         log(f"{name}: graph capture failed: {e!r}")
+    loop = measure_decode_loop(heads, X, V, d, steps) if extras and M == 1 and path == "auto" else None
     ce = measure_ce(heads, X, V, M, steps, warmup, per_graph, path) if extras else None
     topk = measure_topk(heads, X, V, M, steps, warmup, per_graph, path, logits) if extras else None
     sample = measure_sample(heads, X, V, M, steps, warmup, per_graph, logits) if extras else None
@@ -179,6 +180,7 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
         "ce": ce,
         "topk": topk,
         "sample": sample,
+        "decode_loop": loop,
     }
 
 
@@ -209,6 +211,63 @@ def measure_sample(heads, X, V, M, steps, warmup, per_graph, logits, K=16, tempe
     samples = torch.empty((M,), dtype=torch.int32, device="cuda")
     step = lambda i: heads[i % copies].forward_sample_into(X, K, temperature, u, logits, vals, idx, samples)
     return _time_step(step, steps, warmup, per_graph, M, {"K": K, "temperature": temperature})
+
+
+def measure_decode_loop(heads, X0, V, d, steps, K=16, temperature=0.8, per_graph=12):
+    """A synthetic sampling decode loop at M = 1: each step runs the packed
+    head's forward with top-k sampling (archead_forward_sample), and the drawn
+    token picks the next step's hidden state from a seeded bf16 embedding
+    table (a row gather standing in for the rest of the model).  per_graph
+    steps are captured in one HIP graph (uniform numbers drawn beforehand,
+    one per step) and replayed; the head copies rotate as in the other
+    measurements.  The graph's token sequence must equal an eager run's."""
+    import torch
+    copies = len(heads)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    sig = torch.exp(torch.randn((d,), generator=g, device="cuda"))
+    table = (torch.randn((V, d), generator=g, device="cuda") * sig).to(torch.bfloat16)
+    u = torch.rand((per_graph, 1), generator=g, device="cuda")
+    x = torch.empty((1, d), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    vals = torch.empty((1, K), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, K), dtype=torch.int32, device="cuda")
+    toks = torch.empty((per_graph, 1), dtype=torch.int32, device="cuda")
+
+    def run():
+        for t in range(per_graph):
+            heads[t % copies].forward_sample_into(x, K, temperature, u[t], logits, vals, idx, toks[t])
+            torch.index_select(table, 0, toks[t].long(), out=x)
+
+    x.copy_(X0.view(torch.bfloat16))
+    run()
+    torch.cuda.synchronize()
+    eager = toks.clone()
+    side = torch.cuda.Stream()
+    cg = torch.cuda.CUDAGraph()
+    x.copy_(X0.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    with torch.cuda.graph(cg, stream=side):
+        run()
+    x.copy_(X0.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    cg.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(toks, eager))
+    reps = max(1, steps // per_graph)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        cg.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * per_graph)
+    del cg, table
+    return {"K": K, "temperature": temperature, "steps_per_graph": per_graph, "ms_per_token": ms,
+            "tokens_per_s": 1e3 / ms, "graph_tokens_equal_eager": same,
+            "step": "archead_forward_sample (forward, top-k selection and draw in the head's launch where it "
+                    "applies) + embedding-row gather of the drawn token"}
 
 
 def _time_step(step, steps, warmup, per_graph, M, extra):
@@ -434,6 +493,8 @@ def main():
         "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
         "sample": dict(head["sample"], vs_argmax_step=head["sample"]["ms_per_step"] / head["ms_per_step"])
         if extras else None,
+        "decode_loop": dict(head["decode_loop"], vs_argmax_step=head["decode_loop"]["ms_per_token"] / head["ms_per_step"])
+        if extras and head.get("decode_loop") else None,
         "secondary": secondary,
         "baselines": baselines,
     }

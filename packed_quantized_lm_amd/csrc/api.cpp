@@ -76,6 +76,13 @@ struct WsLayout {
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
 int64_t round_m128(int64_t M) { return (M + 127) / 128 * 128; }
 
+// top-k keys the workspace holds: the slice kernel's M x slices x K, or the
+// single launch's per-workgroup lists
+int64_t tkp_keys(const Shape &s, int64_t Mmax)
+{
+    return std::max<int64_t>(std::max<int64_t>(Mmax, 1) * topk_slices(s.V) * kTopKMax, decode_topk_keys(s));
+}
+
 int64_t max_n_part(const Shape &s)
 {
     return std::max<int64_t>(std::max({skinny_max_n_part(s), lds_max_n_part(s), stream2_max_n_part(s)}), 1);
@@ -114,7 +121,7 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     L.tl = off;
     off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * 4);
     L.tkp = off;
-    off = align_up(off + size_t(std::max<int64_t>(Mmax, 1)) * topk_slices(s.V) * kTopKMax * 8);
+    off = align_up(off + size_t(tkp_keys(s, Mmax)) * 8);
     L.sync = off;
     off = align_up(off + kSyncWords * 4);
     L.keys = off;
@@ -184,7 +191,7 @@ Work make_work_in(const Shape &s, void *base, int64_t cap, int64_t M)
     w.lsep = (uint64_t *)(b + L.lsep);
     w.tl = (float *)(b + L.tl);
     w.tkp = (uint64_t *)(b + L.tkp);
-    w.tkp_cap = std::max<int64_t>(cap, 1) * topk_slices(s.V) * kTopKMax;
+    w.tkp_cap = tkp_keys(s, cap);
     w.want_lse = 0;
     w.targets = nullptr;
     w.sync = (uint32_t *)(b + L.sync);
@@ -395,8 +402,10 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
                                    int32_t *argmax, int path, void *hip_stream, hipEvent_t ev0,
                                    hipEvent_t ev1, const int32_t *targets = nullptr,
                                    float *lse = nullptr, float *nll = nullptr, void *ws_ext = nullptr,
-                                   int64_t ws_cap = 0)
+                                   int64_t ws_cap = 0, const DecodeTopk *tk = nullptr, bool *tk_done = nullptr)
 {
+    if (tk_done)
+        *tk_done = false;
     g_err.clear();
     if (!live(h))
         return fail(ARCHEAD_EINVAL, "invalid or freed handle");
@@ -447,10 +456,14 @@ static archead_status forward_impl(archead_t h, int64_t M, const void *X, float 
     w.want_lse = lse ? 1 : 0;
     w.targets = targets;
     const uint16_t *Xb = (const uint16_t *)X;
-    if (one_launch) { // projection, tiles and argmax
+    if (one_launch) { // projection, tiles and argmax (and the top-k selection where it fits)
+        const bool fused_tk = tk && decode_topk_ok(h->dev, M, chosen == ARCHEAD_PATH_SKINNY);
         if (ev0)
             HIP_TRY(hipEventRecord(ev0, st));
-        HIP_TRY(launch_decode(h->dev, w, Xb, logits, argmax, lse, nll, chosen == ARCHEAD_PATH_SKINNY, st));
+        HIP_TRY(launch_decode(h->dev, w, Xb, logits, argmax, lse, nll, chosen == ARCHEAD_PATH_SKINNY, st,
+                              fused_tk ? tk : nullptr));
+        if (tk_done)
+            *tk_done = fused_tk;
         if (ev1)
             HIP_TRY(hipEventRecord(ev1, st));
         return ARCHEAD_OK;
@@ -531,6 +544,28 @@ archead_status archead_forward_ce_path(archead_t h, int64_t M, const void *X, co
     return forward_impl(h, M, X, logits, argmax, path, hip_stream, nullptr, nullptr, targets, lse, nll);
 }
 
+// the forward plus the K largest logits per hidden state (and, with u, one
+// draw from them): inside the single launch where it runs, otherwise the
+// slice and merge kernels over the written logits (and the draw kernel)
+static archead_status topk_impl(archead_t h, int64_t M, const void *X, int32_t K, float *logits, float *values,
+                                int32_t *indices, int path, void *hip_stream, const float *u, float temperature,
+                                int32_t *samples)
+{
+    // the same scale the separate draw kernel takes (launch_topk_sample)
+    const float scale = u ? 1.44269504088896340736f / temperature : 0.f;
+    DecodeTopk tk{K, values, indices, u, scale, samples};
+    bool done = false;
+    archead_status st = forward_impl(h, M, X, logits, nullptr, path, hip_stream, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, 0, &tk, &done);
+    if (st != ARCHEAD_OK || M == 0 || done)
+        return st;
+    Work w = make_work(h, M);
+    HIP_TRY(launch_topk(w, logits, h->s.V, K, values, indices, (hipStream_t)hip_stream));
+    if (u)
+        HIP_TRY(launch_topk_sample(values, indices, M, K, temperature, u, samples, (hipStream_t)hip_stream));
+    return ARCHEAD_OK;
+}
+
 archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, int32_t K, float *logits,
                                         float *values, int32_t *indices, int path, void *hip_stream)
 {
@@ -541,12 +576,7 @@ archead_status archead_forward_topk_path(archead_t h, int64_t M, const void *X, 
         return fail(ARCHEAD_EINVAL, "invalid or freed handle");
     if (K < 1 || K > kTopKMax || int64_t(K) > h->s.V)
         return fail(ARCHEAD_EINVAL, "K must satisfy 1 <= K <= min(" + std::to_string(kTopKMax) + ", V)");
-    archead_status st = forward_impl(h, M, X, logits, nullptr, path, hip_stream, nullptr, nullptr);
-    if (st != ARCHEAD_OK || M == 0)
-        return st;
-    Work w = make_work(h, M);
-    HIP_TRY(launch_topk(w, logits, h->s.V, K, values, indices, (hipStream_t)hip_stream));
-    return ARCHEAD_OK;
+    return topk_impl(h, M, X, K, logits, values, indices, path, hip_stream, nullptr, 0.f, nullptr);
 }
 
 archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int32_t K, float temperature,
@@ -561,12 +591,13 @@ archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int
         return fail(ARCHEAD_EINVAL, "temperature must be positive and finite, with log2(e) / temperature finite");
     if (!u || !samples)
         return fail(ARCHEAD_EINVAL, "u and samples are required");
-    archead_status st =
-        archead_forward_topk_path(h, M, X, K, logits, values, indices, ARCHEAD_PATH_AUTO, hip_stream);
-    if (st != ARCHEAD_OK || M == 0)
-        return st;
-    HIP_TRY(launch_topk_sample(values, indices, M, K, temperature, u, samples, (hipStream_t)hip_stream));
-    return ARCHEAD_OK;
+    if (!logits || !values || !indices)
+        return fail(ARCHEAD_EINVAL, "logits, values and indices are required");
+    if (!live(h))
+        return fail(ARCHEAD_EINVAL, "invalid or freed handle");
+    if (K < 1 || K > kTopKMax || int64_t(K) > h->s.V)
+        return fail(ARCHEAD_EINVAL, "K must satisfy 1 <= K <= min(" + std::to_string(kTopKMax) + ", V)");
+    return topk_impl(h, M, X, K, logits, values, indices, ARCHEAD_PATH_AUTO, hip_stream, u, temperature, samples);
 }
 
 archead_status archead_forward_topk(archead_t h, int64_t M, const void *X, int32_t K, float *logits,

@@ -103,7 +103,32 @@ struct DecodeArgs {
                      // streaming waves compute the columns themselves)
     int nwg;         // streaming workgroups, after them
     unsigned lds_sa, lds_x, lds_ts, lds_xs; // byte offsets of the sA/sC, X, t/s and group-sum regions (sr at 0)
+    // top-k selection in the same launch (tk_K > 0): each streaming wave
+    // writes the largest argmax key of its rows to tkw[m][wave] (and the
+    // logits); the last workgroup selects the K largest logits of each
+    // hidden state into tk_vals / tk_idx [MF][K] and, with tk_u, draws one of
+    // them per hidden state at the temperature whose log2(e) / tau is
+    // tk_scale into tk_samples
+    int tk_K, tk_L;  // K, and wave keys per thread of the final selection (<= kTkKeys)
+    uint64_t *tkw;
+    float *tk_vals;
+    int32_t *tk_idx;
+    const float *tk_u;
+    float tk_scale;
+    int32_t *tk_samples;
+    unsigned lds_tk; // byte offset of the selection's LDS region
 };
+
+// The final selection reads every wave's key, kTkKeys per thread of the
+// last workgroup (all loads in flight at once), so it covers up to
+// 64 kTkKeys workgroups.
+constexpr int kTkKeys = 12;
+// selection LDS: [0, 256) selected keys, per-wave bounds, counters; then the
+// threads' maxima [256]; then the wave keys at or above the bound, at most
+// 4 K Q (Q = wave keys per thread; at most K threads of a wave hold a
+// maximum at or above that wave's bound), and the candidate rows, at most
+// K NV 16, each with two spare slots
+constexpr unsigned kTkMiscBytes = 256;
 
 // log-sum-exp summaries each lane of the last workgroup loads at once, and
 // the bits of the empty summary (-inf, 0)
@@ -144,6 +169,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[4][MF];
     __shared__ LsePart lred[4][MF];
+    __shared__ int s_last; // this workgroup is the last one counted (top-k selection)
     const uint16_t *s_sr = (const uint16_t *)smem;
     const uint16_t *s_x = (const uint16_t *)(smem + a.lds_x);
 
@@ -351,7 +377,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // resolves the argmax and the log-normaliser and bumps the call counter
     // -- comes after every workgroup of the grid, and the bump after every
     // workgroup's read of the counter at its start.
-    auto count_and_finish = [&](bool with_keys) __attribute__((always_inline)) {
+    // (wave 0) count this workgroup; true for the last workgroup of the grid
+    auto count_wg = [&](bool with_keys) __attribute__((always_inline)) -> bool {
         const int nall = a.ntwg + a.nwg;
         const int nslot = nall < kSyncGroups ? nall : kSyncGroups;
         const int slot = (int)(blockIdx.x % nslot);
@@ -375,7 +402,18 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 __hip_atomic_store(sync + sync_slot_done(slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 prev2 = __hip_atomic_fetch_add(sync + sync_top_done(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            if ((uint32_t)__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1)) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane(prev2) == (uint32_t)(nslot - 1);
+        }
+        return false;
+    };
+    // (wave 0 of the last workgroup) the argmax and the log-normaliser from
+    // every workgroup's keys and summaries; counters back to zero for the
+    // next call, which the call counter then tags
+    auto resolve_final = [&]() __attribute__((always_inline)) {
+        const int nall = a.ntwg + a.nwg;
+        const int nslot = nall < kSyncGroups ? nall : kSyncGroups;
+        {
+            {
                 if (a.argmax) {
                     // lane s * MF + m takes (and clears) key m of slot s
                     const int s = lane / MF, m = lane % MF;
@@ -428,6 +466,180 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                     __hip_atomic_fetch_add(sync + sync_epoch(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
+        }
+    };
+    auto count_and_finish = [&](bool with_keys) __attribute__((always_inline)) {
+        if (count_wg(with_keys))
+            resolve_final();
+    };
+
+    // ---- top-k selection (tk_K > 0) ----
+    // Every streaming wave leaves the largest key of its rows in tkw (one key
+    // per wave and hidden state) and its logits in memory.  Let T be the K-th
+    // largest of those wave keys: K distinct logit keys reach T, so each of
+    // the K largest logit keys is at least T, and a wave whose largest key is
+    // below T holds none of them.  The last workgroup therefore
+    //   1. loads the wave keys, thread t keys t, t + 256, ... (tk_L of them,
+    //      all in flight at once);
+    //   2. takes in each wave the K-th largest of its threads' maxima: the
+    //      largest of the four, B, is at most T (K distinct wave keys reach it);
+    //   3. gathers the wave keys at or above B into LDS (at most K threads per
+    //      wave hold one, so at most 4 K tk_L keys) and ranks them: the K
+    //      largest name the source waves, the K-th of them is T;
+    //   4. loads the logits of the source waves (K NV 16 rows at most) and
+    //      gathers the keys at or above T;
+    //   5. ranks those: the K largest, in order.
+    // With fewer than K nonzero wave keys (tiny heads) T is 0 and every row
+    // of every wave is a candidate.
+    //
+    // The K largest of n unique nonzero keys in LDS, to out[0, K) in
+    // descending order (zeros past n), by all 256 threads: with n <= 256 each
+    // thread ranks one key against all n; beyond that wave 0 takes K rounds
+    // of a wave maximum below the previous winner.
+    auto select_k = [&](const uint64_t *s, uint32_t n, uint64_t *out) __attribute__((always_inline)) {
+        const int K = a.tk_K;
+        const uint32_t t = threadIdx.x;
+        if (n <= 256) {
+            if (t < n) {
+                const uint64_t c = s[t];
+                uint32_t rank = 0;
+                for (uint32_t j = 0; j < n; j += 2) {
+                    const uint64_t s0 = s[j], s1 = s[j + 1];
+                    rank += s0 > c ? 1u : 0u;
+                    rank += (j + 1 < n && s1 > c) ? 1u : 0u;
+                }
+                if (rank < (uint32_t)K)
+                    out[rank] = c;
+            } else if (t < (uint32_t)K) {
+                out[t] = 0;
+            }
+        } else if (wv == 0) {
+            uint64_t win = 0;
+            for (int r = 0; r < K; ++r) {
+                uint64_t best = 0;
+                for (uint32_t q = lane; q < n; q += 64) {
+                    const uint64_t k = s[q];
+                    best = ((r == 0 || k < win) && k > best) ? k : best;
+                }
+                win = wave_max_u64(best);
+                if (lane == 0)
+                    out[r] = win;
+            }
+        }
+        __syncthreads();
+    };
+    auto topk_resolve = [&]() __attribute__((always_inline)) {
+        constexpr int SI = (kTopKMax * NV * kVB + 255) / 256; // rows of the source waves per thread
+        const int K = a.tk_K, Q = a.tk_L;
+        const int64_t nw = (int64_t)a.nwg * 4;
+        uint64_t *const s_win = (uint64_t *)(smem + a.lds_tk);            // [16] selected keys
+        uint64_t *const s_bnd = s_win + 16;                               // [4] per-wave bounds
+        uint32_t *const s_cnt = (uint32_t *)(s_win + 20);                 // [2] gather counters
+        uint64_t *const s_tm = (uint64_t *)(smem + a.lds_tk + kTkMiscBytes); // [256] thread maxima
+        uint64_t *const s_wk = s_tm + 256;                                // [4 K Q + 2] wave keys >= B
+        const uint32_t cap1 = 4u * (uint32_t)K * (uint32_t)Q;
+        uint64_t *const s_cand = s_wk + cap1 + 2;                         // [K NV 16 + 2] candidates
+        const uint32_t cap2 = (uint32_t)K * NV * kVB;
+        const int t = threadIdx.x;
+        for (int m = 0; m < MF; ++m) {
+            if (t < 2)
+                s_cnt[t] = 0;
+            if (lane == 0)
+                s_bnd[wv] = 0;
+            // 1.
+            uint64_t kk[kTkKeys];
+            uint64_t tmax = 0;
+#pragma unroll
+            for (int i = 0; i < kTkKeys; ++i) {
+                const int64_t g = t + 256 * i;
+                const bool ok = i < Q && g < nw;
+                kk[i] = __hip_atomic_load(a.tkw + (ok ? m * nw + g : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int i = 0; i < kTkKeys; ++i) {
+                const bool ok = i < Q && (int64_t)(t + 256 * i) < nw;
+                kk[i] = ok ? kk[i] : 0;
+                tmax = umax64(tmax, kk[i]);
+            }
+            s_tm[t] = tmax;
+            __syncthreads();
+            // 2.
+            {
+                const uint64_t *w = s_tm + wv * 64;
+                uint32_t rank = 0;
+                for (int j = 0; j < 64; j += 2) {
+                    const uint64_t s0 = w[j], s1 = w[j + 1];
+                    rank += (s0 > tmax ? 1u : 0u) + (s1 > tmax ? 1u : 0u);
+                }
+                if (tmax != 0 && rank == (uint32_t)(K - 1))
+                    s_bnd[wv] = tmax;
+            }
+            __syncthreads();
+            // 3.
+            const uint64_t B = umax64(umax64(s_bnd[0], s_bnd[1]), umax64(s_bnd[2], s_bnd[3]));
+#pragma unroll
+            for (int i = 0; i < kTkKeys; ++i)
+                if (kk[i] != 0 && kk[i] >= B) {
+                    const uint32_t slot = atomicAdd(s_cnt, 1u);
+                    if (slot < cap1)
+                        s_wk[slot] = kk[i];
+                }
+            __syncthreads();
+            select_k(s_wk, s_cnt[0] < cap1 ? s_cnt[0] : cap1, s_win);
+            // 4.
+            const uint64_t T = s_win[K - 1];
+            float y[SI];
+            int64_t row[SI];
+#pragma unroll
+            for (int i = 0; i < SI; ++i) {
+                const int it = t + 256 * i;
+                const int src = it / (NV * kVB);
+                const uint64_t wk = src < K ? s_win[src] : 0;
+                const int64_t gws = (int64_t)((0xFFFFFFFFu - (uint32_t)wk) / kVB) / NV;
+                row[i] = wk != 0 ? gws * NV * kVB + (it - src * NV * kVB) : V;
+                y[i] = __hip_atomic_load(a.logits + m * V + (row[i] < V ? row[i] : 0), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int i = 0; i < SI; ++i)
+                if (row[i] < V) {
+                    const uint64_t key = argmax_key(y[i], (uint32_t)row[i]);
+                    if (key >= T) {
+                        const uint32_t slot = atomicAdd(s_cnt + 1, 1u);
+                        if (slot < cap2)
+                            s_cand[slot] = key;
+                    }
+                }
+            __syncthreads();
+            // 5.
+            select_k(s_cand, s_cnt[1] < cap2 ? s_cnt[1] : cap2, s_win);
+            if (wv == 0) {
+                if (lane < K) {
+                    const uint64_t k = s_win[lane];
+                    a.tk_idx[m * K + lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+                    a.tk_vals[m * K + lane] = key_value(k);
+                }
+                if (a.tk_u && lane == 0) {
+                    // candidate j weighs 2^((v_j - v_0) log2(e) / tau); the draw
+                    // is the first j whose running sum exceeds u times the total
+                    float v[16], cum[16], c = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        v[j] = key_value(s_win[j < K ? j : K - 1]);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        c += j < K ? __builtin_amdgcn_exp2f((v[j] - v[0]) * a.tk_scale) : 0.f;
+                        cum[j] = c;
+                    }
+                    const float tu = a.tk_u[m] * c;
+                    int pick = K - 1;
+#pragma unroll
+                    for (int j = 15; j >= 0; --j)
+                        pick = (j < K && cum[j] > tu) ? j : pick;
+                    a.tk_samples[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)s_win[pick]);
+                }
+            }
+            __syncthreads(); // the next hidden state reuses the LDS
         }
     };
 
@@ -520,6 +732,20 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             }
         }
         __syncthreads(); // every column of this workgroup is published
+        if (a.tk_K) { // the last workgroup counted runs the selection with all its waves
+            if (wv == 0) {
+                const bool last = count_wg(false);
+                if (lane == 0)
+                    s_last = last ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_last) {
+                topk_resolve();
+                if (wv == 0)
+                    resolve_final();
+            }
+            return;
+        }
         if (wv == 0)
             count_and_finish(false);
         return;
@@ -950,7 +1176,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 y += __shfl_xor(y, 16);
                 y += __shfl_xor(y, 32);
             }
-            yv[v][m] = y;
+            yv[v][m] = y + 0.0f; // -0 stored as +0, as the keys order it
             if (row < V)
                 key[m] = umax64(key[m], argmax_key(y, (uint32_t)row));
         }
@@ -1011,9 +1237,44 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         }
         wait_vm_all();
     }
-    // every wave of the workgroup is past its last use of the counters and
-    // has its keys in LDS
+    // top-k: the wave's largest key of each hidden state (rows in lanes
+    // 0..15) and its logits, with device-scope stores complete before the
+    // workgroup is counted (the last workgroup reads both)
+    if (a.tk_K) {
+        const int64_t nw = (int64_t)a.nwg * 4;
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            const uint64_t kk = umax16_u64(key[m]);
+            if (lane == 0)
+                __hip_atomic_store(a.tkw + m * nw + bid * 4 + wv, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+                if (row < V && lq == 0)
+                    __hip_atomic_store(a.logits + m * V + row, yv[v][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vm_all();
+    }
+    // every wave of the workgroup is past its last use of the counters (and
+    // its top-k stores are complete)
     __syncthreads();
+    if (a.tk_K) {
+        if (wv == 0) {
+            const bool last = count_wg(true);
+            if (lane == 0)
+                s_last = last ? 1 : 0;
+        }
+        __syncthreads();
+        if (s_last) {
+            topk_resolve();
+            if (wv == 0)
+                resolve_final();
+        }
+        return;
+    }
     if (wv != 0) {
         store_logits();
         return;
@@ -1032,11 +1293,17 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 static size_t dal16(size_t x) { return (x + 15) / 16 * 16; }
 
 struct DecodeLds {
-    unsigned sa, x, ts, xs;
+    unsigned sa, x, ts, xs, tk;
     size_t total;
 };
 
-static DecodeLds decode_lds(const Shape &s, int64_t M)
+// streaming workgroups of the single launch for M hidden states
+static int64_t decode_nwg(const Shape &s, int64_t M) { return (s.nvb() + 4 * decode_nv((int)M) - 1) / (4 * decode_nv((int)M)); }
+
+// wave keys per thread of the last workgroup's top-k selection
+static int decode_tk_keys(const Shape &s, int64_t M) { return (int)((decode_nwg(s, M) + 63) / 64); }
+
+static DecodeLds decode_lds(const Shape &s, int64_t M, int K = 0)
 {
     DecodeLds L;
     L.sa = (unsigned)dal16(size_t(4) * decode_nv((int)M) * s.G() * kVB * 2);
@@ -1044,6 +1311,10 @@ static DecodeLds decode_lds(const Shape &s, int64_t M)
     L.ts = (unsigned)(L.x + dal16(size_t(M) * s.d * 2));
     L.xs = (unsigned)dal16(L.ts + size_t(4) * 2 * M * (s.kpad() + s.rpad()) * 2);
     L.total = L.xs + size_t(4) * M * s.G() * 4;
+    L.tk = (unsigned)dal16(L.total);
+    if (K > 0)
+        L.total = L.tk + kTkMiscBytes + 256 * 8 + (size_t(4) * K * decode_tk_keys(s, M) + 2) * 8 +
+                  (size_t(K) * decode_nv((int)M) * kVB + 2) * 8;
     return L;
 }
 
@@ -1090,13 +1361,24 @@ static DecodeKernel decode_kernel(const DevHead &h, int64_t M, bool mx)
 
 bool decode_ok(const DevHead &h, int64_t M, bool mx) { return decode_kernel(h, M, mx) != nullptr; }
 
+bool decode_topk_ok(const DevHead &h, int64_t M, bool mx)
+{
+    return decode_ok(h, M, mx) && decode_tk_keys(h.s, M) <= kTkKeys &&
+           decode_lds(h.s, M, 16).total <= 72 * 1024; // two workgroups per compute unit
+}
+
+int64_t decode_topk_keys(const Shape &s) { return int64_t(kDecodeMaxM) * ((s.nvb() + 15) / 16) * 16; }
+
 hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
-                         float *lse, float *nll, bool mx, hipStream_t st)
+                         float *lse, float *nll, bool mx, hipStream_t st, const DecodeTopk *tk)
 {
     const DecodeKernel kern = decode_kernel(h, w.M, mx);
     if (!kern)
         return hipErrorInvalidValue;
-    const DecodeLds L = decode_lds(h.s, w.M);
+    const int K = tk ? tk->K : 0;
+    if (tk && (K < 1 || K > kTopKMax || !decode_topk_ok(h, w.M, mx)))
+        return hipErrorInvalidValue;
+    const DecodeLds L = decode_lds(h.s, w.M, K);
     DecodeArgs a;
     a.h = h;
     a.w = w;
@@ -1124,6 +1406,17 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     a.lds_x = L.x;
     a.lds_ts = L.ts;
     a.lds_xs = L.xs;
+    a.lds_tk = L.tk;
+    a.tk_K = K;
+    a.tk_L = K ? decode_tk_keys(h.s, w.M) : 0;
+    a.tkw = w.tkp;
+    a.tk_vals = tk ? tk->values : nullptr;
+    a.tk_idx = tk ? tk->indices : nullptr;
+    a.tk_u = tk ? tk->u : nullptr;
+    a.tk_scale = tk ? tk->scale : 0.f;
+    a.tk_samples = tk ? tk->samples : nullptr;
+    if (K && w.M * int64_t(a.nwg) * 4 > w.tkp_cap)
+        return hipErrorInvalidValue; // the waves' keys do not fit the workspace
     if (L.total > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
         if (e != hipSuccess)

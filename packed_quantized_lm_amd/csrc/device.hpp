@@ -268,6 +268,45 @@ __device__ __forceinline__ uint64_t umax16_u64(uint64_t k)
     return umax64(k, dpp_move_u64<kDppRowMirror>(k));
 }
 
+// lane src's 64-bit value, in every lane (src uniform)
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// a DPP move applied to the rows in ROWMASK only; the other lanes keep v
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_rows_u64(uint64_t v)
+{
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
+    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
+    return ((uint64_t)h << 32) | l;
+}
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// the largest key of the wave, in every lane: the maximum within each row of
+// 16 lanes, then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31
+// into rows 2 and 3, so that lane 63 holds the wave's maximum
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
+{
+    k = umax16_u64(k);
+    k = umax64(k, dpp_rows_u64<kDppRowBcast15, 0xA>(k));
+    k = umax64(k, dpp_rows_u64<kDppRowBcast31, 0xC>(k));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// the logit an argmax key encodes (the inverse of orderable(); -0 comes back as +0)
+__device__ __forceinline__ float key_value(uint64_t k)
+{
+    const uint32_t h = (uint32_t)(k >> 32);
+    return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+}
+
 // merge of the summaries held by all 64 lanes (every lane gets the result)
 __device__ __forceinline__ LsePart lse_merge64(LsePart p)
 {

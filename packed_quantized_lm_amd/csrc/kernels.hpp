@@ -63,8 +63,22 @@ constexpr int64_t kLdsMinM = 128;
 // log-sum-exp summary into lse (and nll, with w.targets).
 // decode_ok tells whether a shape and M are supported.
 bool decode_ok(const DevHead &h, int64_t M, bool mx);
+// Top-k selection inside the same launch: the K largest logits of each hidden
+// state (values and indices, M x K) and, with u, one draw per hidden state
+// from them at the temperature whose log2(e) / tau is scale.
+struct DecodeTopk {
+    int K;
+    float *values;
+    int32_t *indices;
+    const float *u;  // may be null (no draw)
+    float scale;
+    int32_t *samples;
+};
+bool decode_topk_ok(const DevHead &h, int64_t M, bool mx);
 hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, float *logits, int32_t *argmax,
-                         float *lse, float *nll, bool mx, hipStream_t st);
+                         float *lse, float *nll, bool mx, hipStream_t st, const DecodeTopk *tk = nullptr);
+// keys the single-launch selection writes per hidden state (workspace sizing)
+int64_t decode_topk_keys(const Shape &s);
 
 // a3 (and the log-normaliser): reduce each row's argmax partial keys to an
 // index (argmax not null) and its log-sum-exp summaries to lse and, with

@@ -25,30 +25,6 @@ constexpr int64_t kTkSlice = 64 * kTkPer; // logits per slice (one wave)
 
 int64_t topk_slices(int64_t V) { return (V + kTkSlice - 1) / kTkSlice; }
 
-// a DPP move applied to the rows in ROWMASK only; the other lanes keep v
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t dpp_rows_u64(uint64_t v)
-{
-    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-    const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
-    const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
-    return ((uint64_t)h << 32) | l;
-}
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-// the largest key of the wave, in every lane: the maximum within each row of
-// 16 lanes, then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31
-// into rows 2 and 3, so that lane 63 holds the wave's maximum
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
-{
-    k = umax16_u64(k);
-    k = umax64(k, dpp_rows_u64<kDppRowBcast15, 0xA>(k));
-    k = umax64(k, dpp_rows_u64<kDppRowBcast31, 0xC>(k));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // the largest of N keys held by one lane, as a tree (short dependency chain)
 template <int N>
 __device__ __forceinline__ uint64_t lane_max(const uint64_t (&k)[N])

@@ -65,6 +65,18 @@ CASES = [
     ("lds", 5000, 256, 16, 4, 32, 129, 1),
     ("skinny", 300000, 128, 1, 1, 32, 2, 16),   # merge over more keys than registers hold (LDS)
     ("skinny", 400000, 128, 1, 1, 32, 1, 16),   # ... and than LDS holds (read each round)
+    # selection inside the single launch (M <= 2, d a multiple of 512): one
+    # workgroup, a few, and more waves than the selecting workgroup has
+    # threads (5, 6 and 9 wave keys per thread at V = 90000 and 140000)
+    ("gemv", 20, 512, 8, 4, 128, 1, 16),
+    ("gemv", 20, 512, 8, 4, 128, 2, 16),
+    ("skinny", 1, 512, 1, 1, 128, 1, 1),
+    ("skinny", 6001, 1024, 40, 20, 128, 1, 16),
+    ("gemv", 6001, 1024, 40, 20, 128, 2, 3),
+    ("skinny", 90000, 512, 16, 8, 128, 1, 16),
+    ("gemv", 90000, 512, 16, 8, 128, 2, 16),
+    ("gemv", 90000, 512, 16, 8, 32, 1, 11),
+    ("gemv", 140000, 512, 16, 8, 128, 2, 16),
 ]
 
 
@@ -84,9 +96,12 @@ def test_topk_matches_oracle(case):
 
 def test_topk_ties_resolve_to_lower_indices():
     # all-zero hidden states: every logit is 0 and the top K are rows 0 .. K-1
-    for path, M in [("gemv", 1), ("skinny", 5), ("lds", 130)]:
-        say(f"topk ties path={path}")
-        f = random_small_head(3000, 512, 32, 8, 128, M, seed=4)
+    # (inside the single launch: more than 256 candidate rows reach the
+    # K-th largest wave key)
+    for path, M, V in [("gemv", 1, 3000), ("gemv", 2, 3000), ("skinny", 1, 3000), ("skinny", 5, 3000),
+                       ("lds", 130, 3000), ("gemv", 1, 90000), ("gemv", 2, 140000)]:
+        say(f"topk ties path={path} M={M} V={V}")
+        f = random_small_head(V, 512, 32, 8, 128, M, seed=4)
         f["X"][:] = 0
         h = load(f)
         v, i, y = gpu_topk(h, f["X"], 16, path=path)
