@@ -285,6 +285,59 @@ archead_status archead_forward_sample(archead_t h, int64_t M, const void *X, int
                                       int32_t *samples, void *hip_stream);
 
 /*
+ * archead_build -- construct a packed head on the GPU from a dense head W
+ * and calibration hidden states H (ARCHead paper section 3.4, the
+ * construction algorithm with inputs W, H, r_c, r_r, g, p, lambda; its steps
+ * are equations 2-5 and the INT8 text after eq 7):
+ *   C = H^T H / N, C_lambda = C + lambda mean(diag C) I, T_p = C_lambda^p (eq 2);
+ *   rank-k core A_c B_c of W by randomized SVD, sqrt(S) to each side;
+ *   A5 = Q5(A_c), B8 = Q8(B_c) (row scales); R4 = SC4(W - A_c B_c) with
+ *   (row, g-group) scales (eq 3); E = W - W_d;
+ *   randomized rank-r SVD of E T_p: A_w = U_r S_r, B_w = V_r^T T_p^-1 (eqs 4-5);
+ *   C8 = Q8(A_w) (row scales), D8 = Q8(B_w) ((row, g-group) scales).
+ * Every quantiser is symmetric: s = fp16(absmax / qmax) rounded to nearest
+ * even directly from fp64, q = clamp(rint(x / s)); a zero group gets s = 0,
+ * q = 0.  Arithmetic is fp64 throughout (matrix-core GEMMs).
+ *
+ * V, d, k, r, g  as archead_pack_load (d a multiple of 128 up to 65536;
+ *                k, r <= min(V, d, 1008)).  Otherwise ARCHEAD_ESHAPE.
+ * N              calibration rows, N >= 1.
+ * W, H           DEVICE fp64, V x d and N x d row-major (borrowed).
+ * p              the metric power: one of 1/4, 1/2, 3/4, 1 (the powers the
+ *                Newton-Schulz square roots reach); else ARCHEAD_EINVAL.
+ * lambda         damping, > 0.
+ * power_iters    power iterations of both randomized SVDs (0..16).
+ * oversample     extra columns of their Gaussian test matrices (0..64, with
+ *                max(k, r) + oversample <= 1024: the sketch's eigenproblem
+ *                runs in one workgroup); else ARCHEAD_EINVAL.
+ * seed           seed of the test matrices (Philox4x32-10 counters).
+ * A5 .. sD       DEVICE outputs in the canonical host layout of
+ *                archead_pack_load (caller-allocated; the k- and r-term
+ *                fields may be NULL when k = 0 / r = 0).
+ * The call allocates its own working memory and waits for the stream before
+ * returning (construction is not a hot path).  HIP failures -> ARCHEAD_EHIP.
+ */
+archead_status archead_build(int64_t V, int64_t d, int64_t k, int64_t r, int64_t g, int64_t N,
+                             const double *W, const double *H, double p, double lambda,
+                             int power_iters, int oversample, uint64_t seed,
+                             int8_t *A5, uint16_t *sA, int8_t *B8, uint16_t *sB,
+                             uint8_t *R4, uint16_t *sR, int8_t *C8, uint16_t *sC,
+                             int8_t *D8, uint16_t *sD, void *hip_stream);
+
+/*
+ * archead_quantize -- the symmetric quantiser of archead_build alone
+ * (ARCHead paper eq 3's Q_b; the INT8 factors after eq 7): x is DEVICE fp64
+ * rows x cols row-major; each row's consecutive groups of `group` columns get
+ * one fp16 scale s = fp16(absmax / (2^(bits-1) - 1)) and codes
+ * q = clamp(rint(x / s), -2^(bits-1), 2^(bits-1) - 1) (s = 0, q = 0 for an
+ * all-zero group).  q: DEVICE int8 rows x cols; s: DEVICE uint16 (fp16 bits)
+ * rows x cols/group.  2 <= bits <= 8 and group dividing cols, else
+ * ARCHEAD_EINVAL.  Enqueued on hip_stream, not waited for.
+ */
+archead_status archead_quantize(const double *x, int64_t rows, int64_t cols, int bits, int64_t group,
+                                int8_t *q, uint16_t *s, void *hip_stream);
+
+/*
  * archead_packed_bytes -- eq 10 of the ARCHead paper: the sum over the
  * registered packed buffers of numel x element size (A5 counted at 5 bits,
  * R4 at 4 bits, int8 fields at 8, scales at 16; each buffer rounded up to a

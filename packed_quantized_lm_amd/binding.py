@@ -38,6 +38,9 @@ SIGNATURES = {
     "archead_forward_sample": (ctypes.c_int, [_VP, _I64, _VP, ctypes.c_int32, ctypes.c_float, _VP, _VP, _VP, _VP,
                                               _VP, _VP]),
     "archead_forward_ce_path": (ctypes.c_int, [_VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int, _VP]),
+    "archead_build": (ctypes.c_int, [_I64] * 6 + [_VP, _VP, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_uint64] + [_VP] * 10 + [_VP]),
+    "archead_quantize": (ctypes.c_int, [_VP, _I64, _I64, ctypes.c_int, _I64, _VP, _VP, _VP]),
     "archead_packed_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_uint64)]),
     "archead_free": (ctypes.c_int, [_VP]),
@@ -327,6 +330,56 @@ class PackedHead:
             self.close()
         except Exception:
             pass
+
+
+def quantize(x, bits: int, group: int | None = None, stream=None):
+    """archead_quantize on a DEVICE fp64 rows x cols tensor: (codes int8,
+    fp16 scale bits as int16) torch tensors; group=None means one group per row."""
+    import torch
+    rows, cols = (int(n) for n in x.shape)
+    group = cols if group is None else int(group)
+    if cols % group:
+        raise ValueError("group must divide the row length")
+    _need(x, "x", (torch.float64,), (rows, cols), x.device)
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty((rows, cols // group), dtype=torch.int16, device=x.device)
+    _check(load_library().archead_quantize(ctypes.c_void_p(x.data_ptr()), rows, cols, int(bits), group,
+                                           ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(s.data_ptr()),
+                                           _stream_handle(stream)), "archead_quantize")
+    return q, s
+
+
+def build_head(W, H, k: int, r: int, g: int, p: float = 0.75, lam: float = 1e-2, power_iters: int = 2,
+               oversample: int = 16, seed: int = 0, stream=None) -> dict:
+    """archead_build on DEVICE fp64 tensors W (V x d) and H (N x d); returns the
+    packed fields in the canonical host layout (numpy), as archead_pack_load takes them."""
+    import torch
+    V, d = (int(n) for n in W.shape)
+    N = int(H.shape[0])
+    _need(W, "W", (torch.float64,), (V, d), W.device)
+    _need(H, "H", (torch.float64,), (N, d), W.device)
+    dev = W.device
+    G = d // g if g and d % g == 0 else 0
+    out = {
+        "A5": torch.empty((V, k), dtype=torch.int8, device=dev), "sA": torch.empty((V,), dtype=torch.int16, device=dev),
+        "B8": torch.empty((k, d), dtype=torch.int8, device=dev), "sB": torch.empty((k,), dtype=torch.int16, device=dev),
+        "R4": torch.empty((V, d // 2), dtype=torch.uint8, device=dev),
+        "sR": torch.empty((V, G), dtype=torch.int16, device=dev),
+        "C8": torch.empty((V, r), dtype=torch.int8, device=dev), "sC": torch.empty((V,), dtype=torch.int16, device=dev),
+        "D8": torch.empty((r, d), dtype=torch.int8, device=dev),
+        "sD": torch.empty((r, G), dtype=torch.int16, device=dev),
+    }
+    order = ["A5", "sA", "B8", "sB", "R4", "sR", "C8", "sC", "D8", "sD"]
+    ptrs = [ctypes.c_void_p(out[n].data_ptr()) if out[n].numel() else None for n in order]
+    _check(load_library().archead_build(V, d, int(k), int(r), int(g), N, ctypes.c_void_p(W.data_ptr()),
+                                        ctypes.c_void_p(H.data_ptr()), float(p), float(lam), int(power_iters),
+                                        int(oversample), int(seed) & (2 ** 64 - 1), *ptrs, _stream_handle(stream)),
+           "archead_build")
+    fields = {"V": V, "d": d, "k": int(k), "r": int(r), "g": int(g)}
+    for n in order:
+        a = out[n].cpu().numpy()
+        fields[n] = a.view(np.uint16) if n.startswith("s") else a
+    return fields
 
 
 def x_tensor_from_bits(bits: np.ndarray, device="cuda"):
