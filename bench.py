@@ -85,6 +85,57 @@ def read_traffic(kernel_tag, workload):
     return data.get("hbm_bytes_per_launch")
 
 
+def _read_sclk_mhz():
+    """The current shader clock of each AMD GPU the host exposes, in MHz, from
+    the driver's DPM table (the level marked '*'); [] where it cannot be read."""
+    import glob
+    out = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as fh:
+                if fh.read().strip() != "0x1002":
+                    continue
+            with open(os.path.join(dev, "pp_dpm_sclk")) as fh:
+                for line in fh:
+                    if "*" in line:
+                        out.append(float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")))
+        except (OSError, ValueError, IndexError):
+            continue
+    return out
+
+
+class SclkSampler:
+    """Polls the shader clock every 2 ms on a host thread while the timed
+    region runs (the host thread is otherwise waiting on the GPU)."""
+
+    def __init__(self):
+        import threading
+        self.samples, self._stop = [], threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = _read_sclk_mhz()
+            if v:
+                self.samples.append(max(v))
+            self._stop.wait(0.002)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return {"source": "pp_dpm_sclk (current DPM level)", "n": int(a.size), "min_mhz": float(a.min()),
+                "median_mhz": float(np.median(a)), "max_mhz": float(a.max())}
+
+
 def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=True):
     import torch
     from packed_quantized_lm_amd import PackedHead, x_tensor_from_bits
@@ -120,12 +171,21 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
     timed_ms = start.elapsed_time(stop)
     kern_ms = np.array([evb[i].elapsed_time(eva[i]) for i in range(steps)])
     # the same steps launched back to back with no events between them
+    with SclkSampler() as sclk:
+        start.record()
+        for i in range(steps):
+            heads[i % copies].forward_into(X, logits, arg, path=path)
+        stop.record()
+        torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # one copy only ("hot": the previous step's reads may still sit in the
+    # memory-side cache); reported beside the rotated figure, never as it
     start.record()
     for i in range(steps):
-        heads[i % copies].forward_into(X, logits, arg, path=path)
+        heads[0].forward_into(X, logits, arg, path=path)
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    hot_ms = start.elapsed_time(stop)
     # and replayed from one HIP graph holding `per_graph` consecutive steps
     # (over the rotated head copies), as a decode loop captured in a graph
     # runs them: no host launch between steps
@@ -170,6 +230,8 @@ def measure(name, steps, warmup, copies, path="auto", with_logits=True, extras=T
         "workload": name, "V": V, "d": d, "k": k, "r": r, "g": g, "M": M,
         "ms_per_step": best_ms / steps, "tokens_per_s": M / (best_ms / 1e3 / steps),
         "direct_ms_per_step": total_ms / steps,
+        "hot_same_copy_ms_per_step": hot_ms / steps,
+        "sclk": sclk.summary(),
         "timed_ms_per_step": timed_ms / steps,
         "graph_ms_per_step": None if graph_ms is None else graph_ms / steps,
         "vtile_us_mean": kern_s * 1e6, "vtile_us_p10": float(np.percentile(kern_ms, 10)) * 1e3,
@@ -355,29 +417,40 @@ def measure_ce(heads, X, V, M, steps, warmup, per_graph, path):
             "tokens_per_s": M / (best / 1e3), "writes": "lse and nll only (no logits, no argmax)"}
 
 
-def cpu_baseline(name="qwen_m1", budget_s=15.0):
+def cpu_baseline(name="qwen_m1", budget_s=15.0, one_thread=False):
     """The oracle as it stands (oracle/forward.py, fp64, numpy BLAS) on a
-    bounded sample of vocabulary rows of the workload, scaled to tokens/s."""
-    from threadpoolctl import threadpool_info
+    bounded sample of vocabulary rows of the workload, scaled to tokens/s;
+    with one_thread, BLAS limited to one thread."""
+    from contextlib import nullcontext
 
-    from oracle import forward
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import forward, packer
     from packed_quantized_lm_amd.synth import make_config
 
     c = make_config(name)
+    if "W" in c:   # the small case is a dense head: the oracle's packer makes its fields (not timed)
+        f, _ = packer.pack(c["W"], c["H"], c["k"], c["r"], c["g"], p=0.75, lam=1e-2)
+        c = dict(f, X=c["X"], M=c["M"])
     V, M = c["V"], c["M"]
     block = 8192
     done, t = 0, 0.0
-    while done < V and t < budget_s:
-        rows = np.arange(done, min(V, done + block))
-        t0 = time.perf_counter()
-        forward.forward(c, c["X"], rows=rows)
-        t += time.perf_counter() - t0
-        done += rows.size
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    with threadpool_limits(limits=1) if one_thread else nullcontext():
+        # blocks of rows until the budget is spent or the head is done (a head
+        # done in under a second is run again, so that the timer resolves it)
+        pos = 0
+        while t < budget_s and (done < V or t < 1.0):
+            rows = np.arange(pos, min(V, pos + block))
+            t0 = time.perf_counter()
+            forward.forward(c, c["X"], rows=rows)
+            t += time.perf_counter() - t0
+            done += rows.size
+            pos = (pos + rows.size) % V
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     full_s = t * V / done
     return {"value": M / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{name}: oracle fp64 forward over vocabulary rows 0..{done - 1} of {V} "
-                      f"({t:.1f} s), scaled to the full head"}
+            "sample": f"{name}: oracle fp64 forward over {done} vocabulary rows of {V} "
+                      f"({t:.2f} s{', one BLAS thread' if one_thread else ''}), scaled to the full head"}
 
 
 def copy_calibration(nbytes, steps):
@@ -463,6 +536,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload)
         log(json.dumps(cpu))
+        # one BLAS thread, on the small case, the decode case and the large head
+        cpu["one_thread"] = []
+        for name in ("tiny", "qwen_m1", "large_m8"):
+            one = cpu_baseline(name, budget_s=4.0, one_thread=True)
+            log(json.dumps(one))
+            cpu["one_thread"].append(dict(one, workload=name))
 
     traffic = read_traffic("decode_one_launch", args.workload)
     out = {
@@ -489,6 +568,7 @@ def main():
                      "kernel_us": head["vtile_us_mean"],
                      "bytes_per_launch": head["vtile_bytes"]},
         "cpu_baseline": cpu,
+        "sclk": head["sclk"],
         "ce": dict(head["ce"], vs_argmax_step=head["ce"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
         "topk": dict(head["topk"], vs_argmax_step=head["topk"]["ms_per_step"] / head["ms_per_step"]) if extras else None,
         "sample": dict(head["sample"], vs_argmax_step=head["sample"]["ms_per_step"] / head["ms_per_step"])

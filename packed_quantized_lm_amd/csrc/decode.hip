@@ -123,12 +123,15 @@ struct DecodeArgs {
 // last workgroup (all loads in flight at once), so it covers up to
 // 64 kTkKeys workgroups.
 constexpr int kTkKeys = 12;
-// selection LDS: [0, 256) selected keys, per-wave bounds, counters; then the
+// selection LDS: [0, 256) selected keys, per-wave bounds, counters; [256,
+// 512) partial-rank counters; then the
 // threads' maxima [256]; then the wave keys at or above the bound, at most
 // 4 K Q (Q = wave keys per thread; at most K threads of a wave hold a
 // maximum at or above that wave's bound), and the candidate rows, at most
-// K NV 16, each with two spare slots
-constexpr unsigned kTkMiscBytes = 256;
+// K NV 16, each with kTkSpare slots past its capacity (read, never used, by
+// the ranking's eight-key steps)
+constexpr unsigned kTkSpare = 8;
+constexpr unsigned kTkMiscBytes = 512;
 
 // log-sum-exp summaries each lane of the last workgroup loads at once, and
 // the bits of the empty summary (-inf, 0)
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     const int gsteps = GS ? GS : a.gsteps;
     const int ntask = a.ntask;
     const bool proj_wg = (int)blockIdx.x < a.ntwg;
+    __builtin_amdgcn_s_setprio(3); // lowered by the streaming waves as they go (pace below)
     const int64_t bid = (int64_t)blockIdx.x - a.ntwg; // streaming workgroup index
     const int64_t wg_vb0 = (proj_wg ? 0 : bid) * 4 * NV;
     const int64_t vb0 = wg_vb0 + wv * NV;
@@ -492,21 +496,87 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // With fewer than K nonzero wave keys (tiny heads) T is 0 and every row
     // of every wave is a candidate.
     //
+    // Appends the keys whose predicate holds to s[] (capacity cap; counter
+    // *cnt): one LDS atomic per wave reserves the wave's block, and each lane
+    // writes at the block's start plus the number of earlier items of the
+    // wave (lower item index, then lower lane).
+    auto wave_append = [&](const auto &pr, const auto &key, uint32_t *cnt, uint64_t *s,
+                           uint32_t cap) __attribute__((always_inline)) {
+        constexpr int N = sizeof(pr) / sizeof(pr[0]);
+        uint32_t off[N], run = 0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint64_t bal = __ballot(pr[i]);
+            off[i] = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            run += (uint32_t)__popcll(bal);
+        }
+        if (run == 0)
+            return;
+        uint32_t base = 0;
+        if (lane == 0)
+            base = atomicAdd(cnt, run);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (pr[i] && base + off[i] < cap)
+                s[base + off[i]] = key[i];
+    };
     // The K largest of n unique nonzero keys in LDS, to out[0, K) in
-    // descending order (zeros past n), by all 256 threads: with n <= 256 each
-    // thread ranks one key against all n; beyond that wave 0 takes K rounds
-    // of a wave maximum below the previous winner.
-    auto select_k = [&](const uint64_t *s, uint32_t n, uint64_t *out) __attribute__((always_inline)) {
+    // descending order (zeros past n), by all 256 threads.  A key's rank is
+    // the number of keys above it.  With n <= 64 the comparisons are split
+    // over the four waves (lane c ranks key c against keys j = wave mod 4)
+    // and the partial ranks meet in LDS counters; with n <= 256 each thread
+    // ranks one key against all n; beyond that wave 0 takes K rounds of a
+    // wave maximum below the previous winner.  s_rank[64] is zero on entry
+    // and on exit.
+    auto select_k = [&](const uint64_t *s, uint32_t n, uint64_t *out, uint32_t *s_rank)
+                        __attribute__((always_inline)) {
         const int K = a.tk_K;
         const uint32_t t = threadIdx.x;
-        if (n <= 256) {
+        if (n <= 64) {
+            if ((uint32_t)lane < n) {
+                const uint64_t c = s[lane];
+                uint32_t part = 0;
+#pragma unroll
+                for (uint32_t j0 = 0; j0 < 64; j0 += 16) {
+                    if (j0 >= n)
+                        break;
+                    uint64_t q[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t j = j0 + 4 * i + wv;
+                        q[i] = s[j < n ? j : n - 1];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part += (j0 + 4 * i + wv < n && q[i] > c) ? 1u : 0u;
+                }
+                if (part)
+                    atomicAdd(s_rank + lane, part);
+            }
+            __syncthreads();
+            if (t < n) {
+                const uint32_t rank = s_rank[t];
+                s_rank[t] = 0;
+                if (rank < (uint32_t)K)
+                    out[rank] = s[t];
+            } else if (t < (uint32_t)K) {
+                out[t] = 0;
+            }
+        } else if (n <= 256) {
             if (t < n) {
                 const uint64_t c = s[t];
                 uint32_t rank = 0;
-                for (uint32_t j = 0; j < n; j += 2) {
-                    const uint64_t s0 = s[j], s1 = s[j + 1];
-                    rank += s0 > c ? 1u : 0u;
-                    rank += (j + 1 < n && s1 > c) ? 1u : 0u;
+                // eight keys per step, read together (the arrays keep kTkSpare
+                // slots past their capacity, so the reads stay inside them)
+                for (uint32_t j = 0; j < n; j += 8) {
+                    uint64_t q[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        q[i] = s[j + i];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        rank += (j + i < n && q[i] > c) ? 1u : 0u;
                 }
                 if (rank < (uint32_t)K)
                     out[rank] = c;
@@ -535,12 +605,15 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         uint64_t *const s_win = (uint64_t *)(smem + a.lds_tk);            // [16] selected keys
         uint64_t *const s_bnd = s_win + 16;                               // [4] per-wave bounds
         uint32_t *const s_cnt = (uint32_t *)(s_win + 20);                 // [2] gather counters
+        uint32_t *const s_rank = (uint32_t *)(smem + a.lds_tk + 256);     // [64] partial ranks
         uint64_t *const s_tm = (uint64_t *)(smem + a.lds_tk + kTkMiscBytes); // [256] thread maxima
-        uint64_t *const s_wk = s_tm + 256;                                // [4 K Q + 2] wave keys >= B
+        uint64_t *const s_wk = s_tm + 256;                                // [4 K Q + spare] wave keys >= B
         const uint32_t cap1 = 4u * (uint32_t)K * (uint32_t)Q;
-        uint64_t *const s_cand = s_wk + cap1 + 2;                         // [K NV 16 + 2] candidates
+        uint64_t *const s_cand = s_wk + cap1 + kTkSpare;                  // [K NV 16 + spare] candidates
         const uint32_t cap2 = (uint32_t)K * NV * kVB;
         const int t = threadIdx.x;
+        if (t < 64)
+            s_rank[t] = 0; // ordered before its first use by the barriers below
         for (int m = 0; m < MF; ++m) {
             if (t < 2)
                 s_cnt[t] = 0;
@@ -555,6 +628,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 const bool ok = i < Q && g < nw;
                 kk[i] = __hip_atomic_load(a.tkw + (ok ? m * nw + g : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            // the draw's uniform number, read beside the wave keys (one round
+            // trip for both; an atomic load stays where it is written)
+            const float um = a.tk_u ? __hip_atomic_load(a.tk_u + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
 #pragma unroll
             for (int i = 0; i < kTkKeys; ++i) {
                 const bool ok = i < Q && (int64_t)(t + 256 * i) < nw;
@@ -577,15 +653,15 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             __syncthreads();
             // 3.
             const uint64_t B = umax64(umax64(s_bnd[0], s_bnd[1]), umax64(s_bnd[2], s_bnd[3]));
+            {
+                bool pr[kTkKeys];
 #pragma unroll
-            for (int i = 0; i < kTkKeys; ++i)
-                if (kk[i] != 0 && kk[i] >= B) {
-                    const uint32_t slot = atomicAdd(s_cnt, 1u);
-                    if (slot < cap1)
-                        s_wk[slot] = kk[i];
-                }
+                for (int i = 0; i < kTkKeys; ++i)
+                    pr[i] = kk[i] != 0 && kk[i] >= B;
+                wave_append(pr, kk, s_cnt, s_wk, cap1);
+            }
             __syncthreads();
-            select_k(s_wk, s_cnt[0] < cap1 ? s_cnt[0] : cap1, s_win);
+            select_k(s_wk, s_cnt[0] < cap1 ? s_cnt[0] : cap1, s_win, s_rank);
             // 4.
             const uint64_t T = s_win[K - 1];
             float y[SI];
@@ -600,19 +676,19 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 y[i] = __hip_atomic_load(a.logits + m * V + (row[i] < V ? row[i] : 0), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
             }
+            {
+                bool pr[SI];
+                uint64_t key[SI];
 #pragma unroll
-            for (int i = 0; i < SI; ++i)
-                if (row[i] < V) {
-                    const uint64_t key = argmax_key(y[i], (uint32_t)row[i]);
-                    if (key >= T) {
-                        const uint32_t slot = atomicAdd(s_cnt + 1, 1u);
-                        if (slot < cap2)
-                            s_cand[slot] = key;
-                    }
+                for (int i = 0; i < SI; ++i) {
+                    key[i] = argmax_key(y[i], (uint32_t)(row[i] < V ? row[i] : 0));
+                    pr[i] = row[i] < V && key[i] >= T;
                 }
+                wave_append(pr, key, s_cnt + 1, s_cand, cap2);
+            }
             __syncthreads();
             // 5.
-            select_k(s_cand, s_cnt[1] < cap2 ? s_cnt[1] : cap2, s_win);
+            select_k(s_cand, s_cnt[1] < cap2 ? s_cnt[1] : cap2, s_win, s_rank);
             if (wv == 0) {
                 if (lane < K) {
                     const uint64_t k = s_win[lane];
@@ -631,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                         c += j < K ? __builtin_amdgcn_exp2f((v[j] - v[0]) * a.tk_scale) : 0.f;
                         cum[j] = c;
                     }
-                    const float tu = a.tk_u[m] * c;
+                    const float tu = um * c;
                     int pick = K - 1;
 #pragma unroll
                     for (int j = 15; j >= 0; --j)
@@ -1035,7 +1111,28 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // kc0 + 3) or low-rank pairs pi, pi + 1; the last iteration issues no
     // loads (no load sits under a branch, which would make the compiler copy
     // the prefetch buffers)
+    // Pacing.  The two workgroups that share a compute unit put a wave on
+    // every SIMD each, and the instruction arbiter favours the older wave:
+    // left alone, the first workgroup on each unit finishes long before the
+    // second, which then streams its last quarter with half the unit's loads
+    // in flight.  Each wave starts at the highest priority and drops a level
+    // as it enters each further quarter of its chunk pairs, so that the wave
+    // behind is issued first and the two stay within about a quarter.
+    int pace_lvl = 0;
+    auto pace = [&](int64_t pi) __attribute__((always_inline)) {
+        const int lvl = (int)((4 * pi) / npairs);
+        if (lvl != pace_lvl) {
+            pace_lvl = lvl;
+            if (lvl == 1)
+                __builtin_amdgcn_s_setprio(2);
+            else if (lvl == 2)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
+    };
     auto res_iter = [&](int64_t pi, int64_t kc0, bool load) __attribute__((always_inline)) { // kc0 % 4 == 0
+        pace(pi);
         // each chunk's registers are refilled as soon as the chunk is used,
         // so that close to four chunks stay in flight
         res_chunk(P0.h0, kc0, 0);
@@ -1056,6 +1153,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         __builtin_amdgcn_sched_barrier(0);
     };
     auto lr_iter = [&](int64_t pi) __attribute__((always_inline)) {
+        pace(pi);
         lr_chunk(P0.h0, 2 * pi - c1);
         load_chunk(P0.h0, 2 * pi + 4);
         __builtin_amdgcn_sched_barrier(0);
@@ -1243,18 +1341,18 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     if (a.tk_K) {
         const int64_t nw = (int64_t)a.nwg * 4;
 #pragma unroll
-        for (int m = 0; m < MF; ++m) {
-            const uint64_t kk = umax16_u64(key[m]);
-            if (lane == 0)
-                __hip_atomic_store(a.tkw + m * nw + bid * 4 + wv, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-#pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
             for (int m = 0; m < MF; ++m)
                 if (row < V && lq == 0)
                     __hip_atomic_store(a.logits + m * V + row, yv[v][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            const uint64_t kk = umax16_u64(key[m]);
+            if (lane == 0)
+                __hip_atomic_store(a.tkw + m * nw + bid * 4 + wv, kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         wait_vm_all();
     }
@@ -1313,8 +1411,8 @@ static DecodeLds decode_lds(const Shape &s, int64_t M, int K = 0)
     L.total = L.xs + size_t(4) * M * s.G() * 4;
     L.tk = (unsigned)dal16(L.total);
     if (K > 0)
-        L.total = L.tk + kTkMiscBytes + 256 * 8 + (size_t(4) * K * decode_tk_keys(s, M) + 2) * 8 +
-                  (size_t(K) * decode_nv((int)M) * kVB + 2) * 8;
+        L.total = L.tk + kTkMiscBytes + 256 * 8 + (size_t(4) * K * decode_tk_keys(s, M) + kTkSpare) * 8 +
+                  (size_t(K) * decode_nv((int)M) * kVB + kTkSpare) * 8;
     return L;
 }
 

@@ -14,9 +14,13 @@ logits in memory.  The last workgroup (256 threads) then
   4. reads the logits of the source waves, rows gws NV 16 + i (i < NV 16),
      thread t items t, t + 256, ... < SI 256, and gathers the keys at or
      above T into an LDS array of capacity K NV 16;
-  5. ranks those: the K largest in order (with more than 256 candidates,
-     K rounds of a 64-lane maximum below the previous winner).
-The emulation asserts that neither array overflows its capacity (step 3: at
+  5. ranks those: the K largest in order.
+Ranking n keys: with n <= 64 lane c of each wave compares key c with the
+keys j = wave mod 4 and the four partial ranks are added; with n <= 256
+each thread ranks one key against all n; beyond that K rounds of a 64-lane
+maximum below the previous winner.
+Both arrays keep 8 slots past their capacity, which the ranking's eight-key
+reads may touch.  The emulation asserts that neither array overflows its capacity (step 3: at
 most K threads per wave hold a maximum at or above that wave's bound, each
 with at most Q keys; step 4: at most K source waves of NV 16 rows) and that
 the result equals the oracle's top-k of the same logits (larger value first,
@@ -29,6 +33,7 @@ from oracle.select import top_k
 
 WAVES, LANES, NT, VB = 4, 64, 256, 16
 KMAX = 16
+SPARE = 8        # slots past each LDS array's capacity
 
 
 def orderable(y):
@@ -44,14 +49,37 @@ def keys_of(y, rows):
 def select_k(s, n, K):
     """The K largest of s[0, n) (unique nonzero keys), zeros past n."""
     out = np.zeros(K, dtype=np.uint64)
+    if n <= LANES:
+        # lane c of wave w ranks key c against keys j = w mod 4 (j < n, read
+        # through a clamped index); the partial ranks add up in 64 counters
+        s_rank = np.zeros(LANES, dtype=np.int64)
+        for w in range(WAVES):
+            for lane in range(LANES):
+                if lane < n:
+                    c = s[lane]
+                    part = 0
+                    for j0 in range(0, 64, 16):
+                        if j0 >= n:
+                            break
+                        for i in range(4):
+                            j = j0 + 4 * i + w
+                            q = s[j if j < n else n - 1]
+                            part += int(j < n and q > c)
+                    s_rank[lane] += part
+        for t in range(NT):
+            if t < n:
+                assert t < LANES
+                if s_rank[t] < K:
+                    out[s_rank[t]] = s[t]
+        return out
     if n <= NT:
         for t in range(NT):
             if t < n:
                 c = s[t]
                 rank = 0
-                for j in range(0, n, 2):
-                    assert j + 1 < s.size            # the spare slot past n is readable
-                    rank += int(s[j] > c) + int(j + 1 < n and s[j + 1] > c)
+                for j in range(0, n, 8):              # eight keys read per step
+                    assert j + 7 < s.size             # the spare slots past n are readable
+                    rank += sum(int(j + i < n and s[j + i] > c) for i in range(8))
                 if rank < K:
                     out[rank] = c
     else:
@@ -94,7 +122,7 @@ def resolve(y, tkw, NV, K, QMAX=12):
                 bnd[w] = sl[lane]
     B = bnd.max()
     # 3.
-    s_wk = np.zeros(cap1 + 2, dtype=np.uint64)
+    s_wk = np.zeros(cap1 + SPARE, dtype=np.uint64)
     n1 = 0
     for t in range(NT):
         for i in range(QMAX):
@@ -105,7 +133,7 @@ def resolve(y, tkw, NV, K, QMAX=12):
     win = select_k(s_wk, n1, K)
     T = win[K - 1]
     # 4.
-    s_cand = np.zeros(cap2 + 2, dtype=np.uint64)
+    s_cand = np.zeros(cap2 + SPARE, dtype=np.uint64)
     n2 = 0
     for t in range(NT):
         for i in range(si):
