@@ -16,9 +16,17 @@ Prints ONE JSON line.  Besides the headline numbers it carries:
   roofline      the vocabulary-tile kernel against HBM bandwidth; its time is
                 taken with HIP events recorded by the library on the same
                 stream immediately around that kernel;
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample (and
+                with one BLAS thread on three workloads);
+  sclk          the shader clock observed during the timed loop;
+  ce / topk / sample / decode_loop
+                the cross-entropy, top-k, top-k sampling steps and a
+                graph-captured decode loop at the same M;
+  construction  archead_build on a seeded dense head against the oracle's
+                packer on the same inputs;
   secondary     the same measurement at M=2048 (prefill, MFMA-bound) and the
-                other workloads, with fewer steps.
+                other workloads, with fewer steps;
+  baselines     the naive group-INT4 and SVD8 + INT4 heads on the same kernels.
 """
 from __future__ import annotations
 
@@ -453,6 +461,42 @@ def cpu_baseline(name="qwen_m1", budget_s=15.0, one_thread=False):
                       f"({t:.2f} s{', one BLAS thread' if one_thread else ''}), scaled to the full head"}
 
 
+def measure_build(V=32768, d=1024, k=64, r=16, g=128, n_calib=1024, power_iters=8, oversample=16, reps=3):
+    """Construction of a packed head (archead_build) from a seeded dense head
+    and calibration states, against the oracle's packer on the same inputs
+    (exact SVDs, numpy BLAS on the host): the one construction figure the
+    pages time."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import packer
+    from packed_quantized_lm_amd import build_head
+    from packed_quantized_lm_amd.synth import dense_head
+
+    c = dense_head(V, d, 96, n_calib)
+    W = torch.from_numpy(c["W"]).cuda()
+    H = torch.from_numpy(c["H"]).cuda()
+    args = dict(p=0.75, lam=1e-2, power_iters=power_iters, oversample=oversample, seed=1)
+    build_head(W, H, k, r, g, **args)          # warm-up (code loading, first allocations)
+    torch.cuda.synchronize()
+    gpu = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        build_head(W, H, k, r, g, **args)
+        torch.cuda.synchronize()
+        gpu.append(time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    packer.pack(c["W"], c["H"], k, r, g, p=0.75, lam=1e-2)
+    ora = time.perf_counter() - t0
+    threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+    return {"workload": f"dense head V={V} d={d} (rank-96 signal + noise), k={k} r={r} g={g}, "
+                        f"{n_calib} calibration rows, p=0.75, lambda=1e-2",
+            "gpu_s": float(np.median(gpu)), "gpu_s_all": gpu,
+            "gpu_settings": f"randomized SVDs, {power_iters} power iterations, {oversample} extra columns; "
+                            "includes copying the fields back to the host",
+            "oracle_s": ora, "oracle_cores": int(threads), "oracle": "oracle/packer.py (exact SVDs, fp64)"}
+
+
 def copy_calibration(nbytes, steps):
     """A plain device-to-device copy of nbytes, run steps times: the known
     read and write volume against which the HBM byte counters (FETCH_SIZE,
@@ -532,6 +576,10 @@ def main():
             b["packed_head_ms_per_step_same_M"] = same_m.get(b["M"])
             log(json.dumps(b))
             baselines.append(b)
+    build = None
+    if extras:
+        build = measure_build()
+        log(json.dumps(build))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload)
@@ -575,6 +623,7 @@ def main():
         if extras else None,
         "decode_loop": dict(head["decode_loop"], vs_argmax_step=head["decode_loop"]["ms_per_token"] / head["ms_per_step"])
         if extras and head.get("decode_loop") else None,
+        "construction": build,
         "secondary": secondary,
         "baselines": baselines,
     }

@@ -140,6 +140,22 @@ def tiny_dense(seed: int = _BASE_SEED) -> dict:
     return {"W": P @ Q + N, "H": H, "X": X, "sigma": sigma, **c}
 
 
+def dense_head(V: int, d: int, rank: int, n_calib: int, seed: int = _BASE_SEED,
+               n_outliers: int = 4, outlier_factor: float = 20.0) -> dict:
+    """A dense head and calibration states of any shape, drawn like the tiny
+    configuration: W = P Q + N with P (V x rank), Q (rank x d) ~ N(0, 0.05^2)
+    and N ~ N(0, 0.01^2); n_calib calibration rows with one anisotropic
+    channel-sigma vector (n_outliers outlier channels)."""
+    rng = _rng(seed, 20)
+    P = rng.normal(0.0, 0.05, size=(V, rank))
+    Q = rng.normal(0.0, 0.05, size=(rank, d))
+    W = P @ Q
+    W += rng.normal(0.0, 0.01, size=(V, d))
+    sigma = channel_sigmas(_rng(seed, 21), d, n_outliers, outlier_factor)
+    H = hidden_states(_rng(seed, 22), n_calib, sigma)
+    return {"W": W, "H": H, "V": V, "d": d}
+
+
 def make_config(name: str, M: int | None = None) -> dict:
     """Inputs of one named configuration.
 
