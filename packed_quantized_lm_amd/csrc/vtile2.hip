@@ -1,6 +1,6 @@
 // vtile2.hip -- the vocabulary-tile step for batched decode (2 <= M <= 32,
 // g = 128): a persistent streaming kernel with the hidden states staged in
-// LDS slab by slab.
+// LDS, all at once where they fit, else slab by slab.
 //
 // ARCHead paper, section 3.2, eq 7 with W_d from eq 3 and the INT8 factors
 // of the text after eq 7.  Per vocabulary row v and hidden state m:
@@ -19,12 +19,14 @@
 // bf16 integers, device.hpp).  The A operands -- X, and the bf16 hi/lo parts
 // of t and s -- are read from LDS, where they sit in MFMA fragment order (one
 // 1 KiB block per 16 rows x 32 columns: lane l's 16 bytes at 16 l), so the
-// reads are free of bank conflicts.  t and s are staged once; X is staged
-// in slabs of four K-chunks (512 columns), two slab buffers, the next slab's
-// copy issued a whole slab ahead by the eight waves together and checked
-// at the slab boundary by one wait (the copy is older than the chunk the
-// wave needs next) and one barrier.  The only other vector-memory loads of
-// the loop are the packed codes.
+// reads are free of bank conflicts.  t and s are staged once.  Where all of
+// X fits beside them (one m-tile and d up to about 2560), X is staged once
+// too and the stream has no barrier; otherwise X is staged in slabs of four
+// K-chunks (512 columns), two slab buffers, the next slab's copy issued a
+// whole slab ahead by the eight waves together and checked at the slab
+// boundary by one wait (the copy is older than the chunk the wave needs
+// next) and one barrier.  The only other vector-memory loads of the loop
+// are the packed codes.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -54,14 +56,16 @@ struct Stream2Args {
 // v-block range [lo, hi) of wave gw of W
 __device__ __forceinline__ int64_t wave_lo(int64_t gw, int64_t W, int64_t nvb) { return gw * nvb / W; }
 
-template <int MT, int NV>
+// XF: all of X staged once (when it fits in LDS next to the rest), so the
+// stream needs no barrier; otherwise slab by slab in two buffers.
+template <int MT, int NV, bool XF>
 __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2Args a)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint64_t red[kS2Waves][MT * 16];
     __shared__ LsePart lred[kS2Waves][MT * 16];
     __shared__ int32_t s_tgt[64];
-    uint16_t *const s_x = (uint16_t *)(smem + a.lds_x);   // [2][MT][16][64][8] bf16
+    uint16_t *const s_x = (uint16_t *)(smem + a.lds_x);   // [2][MT][16][64][8] bf16 (XF: [MT][d / 32][64][8])
     uint16_t *const s_ts = (uint16_t *)(smem + a.lds_ts); // t [MT][kst][2][64][8], then s [MT][rst][2][64][8]
     float *const s_xs = (float *)(smem + a.lds_xs);       // [G][MT*16]  -136 sum of X over the group
     uint16_t *const s_sr = (uint16_t *)(smem + a.lds_sr); // [v-blocks of the workgroup][G][16] fp16
@@ -125,7 +129,17 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
             lds_dma16<false>(a.X + r * d + (sl * 16 + kl) * kKStep + 8 * lq, dst + b * 512);
         }
     };
-    copy_slab(0);
+    const int64_t nks = d / kKStep;
+    if constexpr (XF) {
+        // every K-step block of every m-tile, once: block b = mt nks + ks
+        for (int64_t b = wv; b < MT * nks; b += kS2Waves) {
+            const int64_t mt = b / nks, ks = b - (b / nks) * nks;
+            const int64_t r = mt * 16 + lr < M ? mt * 16 + lr : M - 1;
+            lds_dma16<false>(a.X + r * d + ks * kKStep + 8 * lq, s_x + b * 512);
+        }
+    } else {
+        copy_slab(0);
+    }
 
     // ---- the chunk stream: item it = (group it / per, chunk it % per) ----
     const int64_t per = nlr + nkc; // a multiple of kS2NB
@@ -277,13 +291,18 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
         // folded with its scale: acc += sR (sum x (q + 136) - 136 sum x)
         for (int64_t s = 0; s < n_slab; ++s) {
             const int64_t S = j * n_slab + s;
-            // the copy of slab S was issued before the oldest outstanding
-            // chunk load: waiting for that chunk waits for the copy
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((kS2NB - 1) * NV));
-            __syncthreads(); // every wave's part of slab S is in; slab S - 1 is done with
-            if (S + 1 < (int64_t)ngroups * n_slab)
-                copy_slab(S + 1);
-            const uint16_t *xs_base = s_x + (S & 1) * (MT * 16 * 512);
+            const uint16_t *xs_base;
+            if constexpr (XF) {
+                xs_base = s_x + s * 16 * 512; // K-step 16 s of m-tile 0 (m-tile mt: + mt nks blocks)
+            } else {
+                // the copy of slab S was issued before the oldest outstanding
+                // chunk load: waiting for that chunk waits for the copy
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((kS2NB - 1) * NV));
+                __syncthreads(); // every wave's part of slab S is in; slab S - 1 is done with
+                if (S + 1 < (int64_t)ngroups * n_slab)
+                    copy_slab(S + 1);
+                xs_base = s_x + (S & 1) * (MT * 16 * 512);
+            }
 #pragma unroll
             for (int b = 0; b < kS2NB; ++b) {
                 const int64_t kc = s * kS2Slab + b;
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
                     u32x4 xf[MT];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        xf[mt] = *(const u32x4 *)(xs_base + ((mt * 16 + b * 4 + st) * 64 + lane) * 8);
+                        xf[mt] = *(const u32x4 *)(xs_base + (((XF ? mt * nks : mt * 16) + b * 4 + st) * 64 + lane) * 8);
 #pragma unroll
                     for (int v = 0; v < NV; ++v) {
                         const uint32_t wd = st == 0 ? buf[b][v].x : st == 1 ? buf[b][v].y
@@ -404,7 +423,7 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
 }
 
 struct Stream2Plan {
-    bool ok;
+    bool ok, xfull;
     int MT, NV, nwg, ngroups;
     unsigned lds_x, lds_ts, lds_xs, lds_sr;
     size_t lds;
@@ -431,11 +450,15 @@ Stream2Plan stream2_plan(const DevHead &h, int64_t M)
     // range of 8 takes two groups of 4; one m-tile leaves room for more
     p.NV = p.MT == 2 ? (per_wave <= 5 ? 5 : 4) : (per_wave <= 5 ? 5 : 4);
     p.ngroups = (int)((per_wave + p.NV - 1) / p.NV);
-    const size_t x_bytes = size_t(2) * p.MT * 16 * 1024;
     const size_t ts_bytes = size_t(p.MT) * (s.kst() + s.rst()) * 2 * 1024;
     const size_t xs_bytes = size_t(s.G()) * p.MT * 16 * 4;
     // the workgroup's v-block range holds at most 8 per_wave v-blocks
     const size_t sr_bytes = size_t(kS2Waves) * per_wave * s.G() * kVB * 2;
+    const size_t rest = al256(ts_bytes) + al256(xs_bytes) + al256(sr_bytes);
+    // all of X in LDS where it fits (no barrier in the stream), else two slabs
+    const size_t x_full = size_t(p.MT) * (s.d / kKStep) * 1024, x_slabs = size_t(2) * p.MT * 16 * 1024;
+    p.xfull = al256(x_full) + rest <= 150 * 1024;
+    const size_t x_bytes = p.xfull ? x_full : x_slabs;
     p.lds_x = 0;
     p.lds_ts = (unsigned)al256(x_bytes);
     p.lds_xs = (unsigned)(p.lds_ts + al256(ts_bytes));
@@ -446,10 +469,10 @@ Stream2Plan stream2_plan(const DevHead &h, int64_t M)
     return p;
 }
 
-template <int MT, int NV>
+template <int MT, int NV, bool XF>
 hipError_t launch2(const Stream2Args &a, const Stream2Plan &p, hipStream_t st)
 {
-    auto kern = vtile_stream2_kernel<MT, NV>;
+    auto kern = vtile_stream2_kernel<MT, NV, XF>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
     if (e != hipSuccess)
         return e;
@@ -495,9 +518,13 @@ hipError_t launch_vtile_stream2(const DevHead &h, const Work &w, const uint16_t 
     a.lds_ts = p.lds_ts;
     a.lds_xs = p.lds_xs;
     a.lds_sr = p.lds_sr;
+    if (p.MT == 1 && p.xfull)
+        return p.NV == 5 ? launch2<1, 5, true>(a, p, st) : launch2<1, 4, true>(a, p, st);
     if (p.MT == 1)
-        return p.NV == 5 ? launch2<1, 5>(a, p, st) : launch2<1, 4>(a, p, st);
-    return p.NV == 5 ? launch2<2, 5>(a, p, st) : launch2<2, 4>(a, p, st);
+        return p.NV == 5 ? launch2<1, 5, false>(a, p, st) : launch2<1, 4, false>(a, p, st);
+    if (p.xfull)
+        return p.NV == 5 ? launch2<2, 5, true>(a, p, st) : launch2<2, 4, true>(a, p, st);
+    return p.NV == 5 ? launch2<2, 5, false>(a, p, st) : launch2<2, 4, false>(a, p, st);
 }
 
 } // namespace archead
