@@ -70,7 +70,8 @@ bool live(archead_t h)
 }
 
 struct WsLayout {
-    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, lsep, tl, tkp, sync, keys, colflag, total;
+    size_t t16, s16, xsneg, tf32, sf32, xsw, tsw, ssw, xsc, lfill, part, lsep, tl, tkp, sync, keys, colflag, ppart, pcnt,
+        total;
 };
 
 int64_t round_m(int64_t M) { return (M + 31) / 32 * 32; }
@@ -128,6 +129,11 @@ WsLayout ws_layout(const Shape &s, int64_t Mmax)
     off = align_up(off + kKeyWords * 8);
     L.colflag = off;
     off = align_up(off + size_t(std::max<int64_t>(s.k + s.r, 1)) * 4);
+    const int64_t ptiles = std::max<int64_t>((s.k + s.r + 15) / 16, 1);
+    L.ppart = off;
+    off = align_up(off + size_t(ptiles) * kProjKS * 2 * 64 * 4 * 4);
+    L.pcnt = off;
+    off = align_up(off + size_t(ptiles) * 4);
     L.total = off;
     return L;
 }
@@ -197,6 +203,8 @@ Work make_work_in(const Shape &s, void *base, int64_t cap, int64_t M)
     w.sync = (uint32_t *)(b + L.sync);
     w.keys = (uint64_t *)(b + L.keys);
     w.colflag = (uint32_t *)(b + L.colflag);
+    w.ppart = (float *)(b + L.ppart);
+    w.pcnt = (uint32_t *)(b + L.pcnt);
     return w;
 }
 

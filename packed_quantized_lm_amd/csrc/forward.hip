@@ -36,6 +36,8 @@ struct ProjArgs {
     float *tf32, *sf32; // fp32 t and s (large-M projection)
     float *xsneg;
     int ncolblk;
+    float *ppart;   // matrix-core projection for 5 <= M <= 32: slice partial sums
+    uint32_t *pcnt; // and per-tile slice counts (zero between calls)
 };
 
 __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
@@ -145,6 +147,8 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
 
 constexpr int kPSmallM = 4; // largest M of the one-workgroup-per-column projection
 __global__ void proj_small_kernel(ProjArgs a);
+template <int MT>
+__global__ void proj_skinny_mfma_kernel(ProjArgs a);
 
 static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
 {
@@ -168,6 +172,8 @@ static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
     a.tf32 = w.tf32;
     a.sf32 = w.sf32;
     a.xsneg = w.xsneg;
+    a.ppart = w.ppart;
+    a.pcnt = w.pcnt;
     return a;
 }
 
@@ -179,6 +185,14 @@ hipError_t launch_proj(const DevHead &h, const Work &w, const uint16_t *X, hipSt
     // g-group must fall inside one window
     if (w.M <= kPSmallM && (h.s.d <= 4096 || 4096 % h.s.g == 0)) {
         hipLaunchKernelGGL(proj_small_kernel, dim3((unsigned)(ncol + 1)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    if (w.M <= 32 && h.s.d <= 16384) { // matrix cores: a wave per (16 columns, K-slice), then a wave per X row
+        const unsigned grid = (unsigned)((ncol + 15) / 16 * kProjKS + w.M);
+        if (w.M <= 16)
+            hipLaunchKernelGGL(proj_skinny_mfma_kernel<1>, dim3(grid), dim3(64), 0, st, a);
+        else
+            hipLaunchKernelGGL(proj_skinny_mfma_kernel<2>, dim3(grid), dim3(64), 0, st, a);
         return hipGetLastError();
     }
     a.ncolblk = (int)((ncol + 4 * kProjNI - 1) / (4 * kProjNI));
@@ -401,6 +415,184 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
     dim3 grid((unsigned)((ncol + 15) / 16), (unsigned)((w.M + kPMB * 16 - 1) / (kPMB * 16)));
     hipLaunchKernelGGL(proj_mfma_kernel, grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a1 for 5 <= M <= 32 (batched decode): the products on the matrix cores,
+// written as the bf16 hi/lo pairs of the small-M paths.  One wave per (16
+// output columns, K-slice): kProjKS slices of d, so that the grid's loads
+// (whose MFMA fragments touch 16 rows per instruction) spread over about
+// kProjKS times as many compute units as tiles.  Each wave issues its loads
+// up to eight K-steps at a time, stores its partial sums with device-scope
+// stores and counts its tile; the last wave of a tile adds the slices in a
+// fixed order and writes t, s.  Integer weights enter as exact bf16
+// integers; each g-group of a D8 row is accumulated on its own and folded in
+// with its scale (a group split between two slices is folded by both, the
+// same sum).  Waves past the tiles write the per-group X sums, one row each,
+// from coalesced loads.
+// ---------------------------------------------------------------------------
+constexpr int kPSKB = 8;        // K-steps per load batch
+constexpr int kPSMaxD = 16384;  // widest d of the X-sum waves (their LDS row)
+
+template <int MT>
+__global__ __launch_bounds__(64) void proj_skinny_mfma_kernel(ProjArgs a)
+{
+    const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t ncol = a.k + a.r;
+    const int64_t ntile = (ncol + 15) / 16;
+    const int64_t bid = blockIdx.x;
+
+    if (bid >= ntile * kProjKS) { // per-group sums of X for row m
+        __shared__ float s_c[kPSMaxD / 8];
+        const int64_t m = bid - ntile * kProjKS;
+        if (m >= a.M)
+            return;
+        const uint16_t *xr = a.X + m * a.d;
+        const int64_t nch = a.d / 8; // 16-byte chunks of the row
+        for (int64_t p0 = 0; p0 < nch; p0 += 64 * 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t p = p0 + 64 * q + lane;
+                v[q] = p < nch ? *(const u32x4 *)(xr + 8 * p) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int64_t p = p0 + 64 * q + lane;
+                if (p < nch)
+                    s_c[p] = bf_lo(v[q].x) + bf_hi(v[q].x) + bf_lo(v[q].y) + bf_hi(v[q].y) + bf_lo(v[q].z) +
+                             bf_hi(v[q].z) + bf_lo(v[q].w) + bf_hi(v[q].w);
+            }
+        }
+        __syncthreads();
+        const int64_t cpg = a.g / 8;
+        for (int64_t grp = lane; grp < a.G; grp += 64) {
+            float sx = 0.f;
+            for (int64_t p = grp * cpg; p < (grp + 1) * cpg; ++p)
+                sx += s_c[p];
+            a.xsneg[grp * a.Mp + m] = -kR4Bias * sx;
+        }
+        return;
+    }
+
+    const int64_t tile = bid / kProjKS, ks = bid - (bid / kProjKS) * kProjKS;
+    const int64_t c0 = tile * 16;
+    const int64_t c = c0 + lr < ncol ? c0 + lr : ncol - 1;
+    const bool isd = c >= a.k;
+    const int8_t *wrow = (isd ? a.d8 + (c - a.k) * a.d : a.b8 + c * a.d) + 8 * lq;
+    const float *sdrow = a.sd + (isd ? (c - a.k) * a.G : 0);
+    const uint16_t *xr[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = 16 * mt + lr;
+        xr[mt] = a.X + (m < a.M ? m : a.M - 1) * a.d + 8 * lq;
+    }
+    const int64_t nks = a.d / kKStep, gsteps = a.g / kKStep;
+    const int64_t ks0 = ks * nks / kProjKS, ks1 = (ks + 1) * nks / kProjKS;
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[MT], gacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = gacc[mt] = zero;
+    for (int64_t kb = ks0; kb < ks1; kb += kPSKB) {
+        // every load of the batch -- operands and group scales -- before
+        // its first product
+        u32x4 x[kPSKB][MT];
+        u32x2 w[kPSKB];
+        float gs[kPSKB];
+#pragma unroll
+        for (int q = 0; q < kPSKB; ++q) {
+            const int64_t k = kb + q < ks1 ? kb + q : ks1 - 1;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                x[q][mt] = *(const u32x4 *)(xr[mt] + k * kKStep);
+            w[q] = *(const u32x2 *)(wrow + k * kKStep);
+            gs[q] = isd ? sdrow[k / gsteps] : 1.f;
+        }
+#pragma unroll
+        for (int q = 0; q < kPSKB; ++q) {
+            const int64_t k = kb + q;
+            if (k >= ks1)
+                break;
+            const u32x4 bw = i8_bf16(w[q]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                gacc[mt] = mfma_bf16(x[q][mt], bw, gacc[mt]);
+            if ((k + 1) % gsteps == 0 || k + 1 == ks1) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[mt][i] = __builtin_fmaf(gs[q], gacc[mt][i], acc[mt][i]);
+                    gacc[mt] = zero;
+                }
+            }
+        }
+    }
+    // this slice's partial sums, complete before the tile's count
+    float *pp = a.ppart + ((tile * kProjKS + ks) * 2) * 256 + lane * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(pp + mt * 256 + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t prev = 0;
+    if (lane == 0)
+        prev = __hip_atomic_fetch_add(a.pcnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) != (uint32_t)(kProjKS - 1))
+        return;
+    // the last slice of the tile: every slice's partials, in slice order
+    if (lane == 0)
+        __hip_atomic_store(a.pcnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (pairs of floats as 64-bit device-scope loads; half of the slices at a
+    // time, all their loads in flight)
+    const uint64_t *tp = (const uint64_t *)(a.ppart + (tile * kProjKS * 2) * 256 + lane * 4);
+    float v[MT][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint64_t part[kProjKS / 2][MT][2];
+#pragma unroll
+        for (int q = 0; q < kProjKS / 2; ++q)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    part[q][mt][e] = __hip_atomic_load(tp + ((h * (kProjKS / 2) + q) * 2 + mt) * 128 + e,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < kProjKS / 2; ++q)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t pr = part[q][mt][i >> 1];
+                    const float x = __uint_as_float((uint32_t)(i & 1 ? pr >> 32 : pr));
+                    v[mt][i] = (h == 0 && q == 0) ? x : v[mt][i] + x;
+                }
+    }
+    if (c0 + lr >= ncol)
+        return;
+    const float sb = isd ? 1.f : a.sb[c];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = 16 * mt + 4 * lq + i;
+            if (m >= a.M)
+                continue;
+            const float t = v[mt][i] * sb;
+            const uint16_t hi = f32_to_bf16_rne(t);
+            const uint16_t lo = f32_to_bf16_rne(t - __uint_as_float((uint32_t)hi << 16));
+            if (isd) {
+                a.s16[m * a.rpad + (c - a.k)] = hi;
+                a.s16[(a.Mp + m) * a.rpad + (c - a.k)] = lo;
+            } else {
+                a.t16[m * a.kpad + c] = hi;
+                a.t16[(a.Mp + m) * a.kpad + c] = lo;
+            }
+        }
 }
 
 // ---------------------------------------------------------------------------

@@ -133,7 +133,13 @@ struct Work {
     // top-k selection: per (row, 1024-logit slice) the slice's K largest keys
     uint64_t *tkp;          // [M][slices][K]
     int64_t tkp_cap;        // uint64 slots in tkp
+    // matrix-core projection for 5 <= M <= 32: per (16-column tile, K-slice)
+    // partial sums, and per tile a count of slices done (zero between calls)
+    float *ppart;           // [tiles][kProjKS][2][64][4]
+    uint32_t *pcnt;         // [tiles]
 };
+
+constexpr int kProjKS = 16; // K-slices of the matrix-core projection for 5 <= M <= 32
 
 constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path
 
