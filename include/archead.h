@@ -68,6 +68,15 @@ typedef enum archead_status {
     ARCHEAD_EHIP = 5    /* a HIP runtime call failed                        */
 } archead_status;
 
+/* Allocation-failure injection (for tests of callers' error handling): when
+ * the environment variable ARCHEAD_TEST_ALLOC_LIMIT holds a byte count, every
+ * device allocation the library would make above that size -- the packed
+ * block of archead_pack_load, a workspace growth (archead_reserve and the
+ * forward calls), each buffer of archead_build and archead_quantize -- is
+ * refused before any HIP call and the entry point returns ARCHEAD_ENOMEM with
+ * its state unchanged (a handle keeps its old workspace).  The variable is
+ * read at every allocation; unset or empty, it has no effect. */
+
 /* Kernel families for the vocabulary-tile step (archead_forward_path).
  * GEMV runs the whole forward (projection, vocabulary tiles, argmax) as one
  * kernel launch; it takes d a multiple of 512 and M = 1, or M = 2 with

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <set>
@@ -16,6 +17,7 @@
 #include <thread>
 #include <vector>
 
+#include "api_internal.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -155,6 +157,8 @@ archead_status grow_workspace(archead_t h, int64_t M, hipStream_t st)
                                         std::to_string(M) + " would grow it while the stream is "
                                         "capturing: call archead_reserve before the capture");
     WsLayout L = ws_layout(h->s, M);
+    if (archead::alloc_refused(L.total))
+        return fail(ARCHEAD_ENOMEM, "workspace of " + std::to_string(L.total) + " bytes refused (ARCHEAD_TEST_ALLOC_LIMIT)");
     void *p = nullptr;
     hipError_t e = hipMallocAsync(&p, L.total, st);
     if (e != hipSuccess)
@@ -230,6 +234,16 @@ archead_status validate_shape(int64_t V, int64_t d, int64_t k, int64_t r, int64_
 namespace archead {
 
 archead_status api_fail(archead_status s, const std::string &msg) { return fail(s, msg); }
+
+bool alloc_refused(size_t bytes)
+{
+    const char *v = std::getenv("ARCHEAD_TEST_ALLOC_LIMIT");
+    if (!v || !*v)
+        return false;
+    char *end = nullptr;
+    const unsigned long long lim = std::strtoull(v, &end, 10);
+    return end != v && bytes > lim;
+}
 
 archead_status handle_device(archead_t h, int *device)
 {
@@ -307,6 +321,8 @@ archead_status archead_pack_load(int64_t V, int64_t d, int64_t k, int64_t r, int
     const size_t o_sd = place(size_t(r) * s.G() * 4);
     const size_t total = off;
 
+    if (archead::alloc_refused(total))
+        return fail(ARCHEAD_ENOMEM, "packed head of " + std::to_string(total) + " bytes refused (ARCHEAD_TEST_ALLOC_LIMIT)");
     std::vector<char> host;
     try {
         host.assign(total, 0);

@@ -1,5 +1,6 @@
 // api_internal.hpp -- what api.cpp lends to the other host-side entry points
-// of the library (the no-allocation forward in noalloc.hip).
+// of the library (the no-allocation forward in noalloc.hip, the construction
+// in build.hip).
 #pragma once
 #include <string>
 
@@ -9,6 +10,11 @@ namespace archead {
 
 // records msg as the calling thread's last error and returns s
 archead_status api_fail(archead_status s, const std::string &msg);
+
+// Test hook: with ARCHEAD_TEST_ALLOC_LIMIT=<bytes> in the environment, every
+// device allocation of the library larger than that is refused (the caller
+// reports ARCHEAD_ENOMEM, as for a failed hipMalloc) before any HIP call.
+bool alloc_refused(size_t bytes);
 
 // ARCHEAD_OK and the device the handle lives on, or ARCHEAD_EINVAL for a bad handle
 archead_status handle_device(archead_t h, int *device);

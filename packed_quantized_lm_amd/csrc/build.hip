@@ -417,6 +417,12 @@ unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<in
             throw std::string(#expr) + ": " + hipGetErrorString(e_);                           \
     } while (0)
 
+// a device allocation of the construction that failed (or was refused by
+// the ARCHEAD_TEST_ALLOC_LIMIT test hook)
+struct BuildOom {
+    size_t bytes;
+};
+
 // ---------------------------------------------------------------------------
 // host orchestration (device memory from one arena the call allocates)
 // ---------------------------------------------------------------------------
@@ -430,8 +436,10 @@ struct Builder {
     }
     double *alloc(int64_t n)
     {
+        const size_t bytes = (size_t)std::max<int64_t>(n, 1) * sizeof(double);
         void *p = nullptr;
-        BUILD_TRY(hipMalloc(&p, (size_t)std::max<int64_t>(n, 1) * sizeof(double)));
+        if (alloc_refused(bytes) || hipMalloc(&p, bytes) != hipSuccess)
+            throw BuildOom{bytes};
         bufs.push_back(p);
         return (double *)p;
     }
@@ -665,6 +673,8 @@ extern "C" archead_status archead_quantize(const double *x, int64_t rows, int64_
         quantize(b, x, rows, cols, cols, bits, group, q, s, nullptr);
     } catch (const std::string &e) {
         return api_fail(ARCHEAD_EHIP, e);
+    } catch (const BuildOom &e) {
+        return api_fail(ARCHEAD_ENOMEM, "device allocation of " + std::to_string(e.bytes) + " bytes failed");
     }
     return ARCHEAD_OK;
 }
@@ -763,6 +773,8 @@ extern "C" archead_status archead_build(int64_t V, int64_t d, int64_t k, int64_t
         (void)G;
     } catch (const std::string &e) {
         return api_fail(ARCHEAD_EHIP, "construction: " + e);
+    } catch (const BuildOom &e) {
+        return api_fail(ARCHEAD_ENOMEM, "construction: device allocation of " + std::to_string(e.bytes) + " bytes failed");
     }
     return ARCHEAD_OK;
 }

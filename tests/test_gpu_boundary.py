@@ -3,7 +3,8 @@ tensors of the wrong device, type or shape before any launch; the library
 rejects a temperature whose reciprocal overflows; a forward call that must
 grow the workspace does so in stream order (results stay right when calls
 of growing M follow each other without a wait), and refuses to grow while
-its stream is being captured into a graph."""
+its stream is being captured into a graph; a device allocation refused by the
+ARCHEAD_TEST_ALLOC_LIMIT hook comes back as ENOMEM and the handle survives it."""
 import numpy as np
 import pytest
 
@@ -150,4 +151,46 @@ def test_growth_refused_while_capturing():
     torch.cuda.synchronize()
     ref = oracle_forward.forward(f, f["X"])
     assert_logits_close(y.cpu().numpy(), ref, what="after capture")
+    h.close()
+
+
+def test_allocation_failure_is_a_status(monkeypatch):
+    """With ARCHEAD_TEST_ALLOC_LIMIT set, the packed head's block, a workspace
+    growth and the construction's buffers are refused as if the device were out
+    of memory: each call returns ENOMEM, nothing aborts, and the handle keeps
+    its old workspace and works again once the limit is lifted."""
+    import torch
+    from packed_quantized_lm_amd import PackedHead, build_head, x_tensor_from_bits
+    from packed_quantized_lm_amd.binding import ENOMEM, ArcheadError
+    say("allocation failure injected through ARCHEAD_TEST_ALLOC_LIMIT")
+    f = random_small_head(2000, 512, 32, 8, 128, 150, seed=35)
+    monkeypatch.setenv("ARCHEAD_TEST_ALLOC_LIMIT", "1024")
+    with pytest.raises(ArcheadError) as e:
+        PackedHead(f)
+    assert e.value.status == ENOMEM
+    monkeypatch.delenv("ARCHEAD_TEST_ALLOC_LIMIT")
+    h = PackedHead(f)
+    h.reserve(2)
+    X = x_tensor_from_bits(f["X"])
+    y = torch.empty((150, f["V"]), dtype=torch.float32, device=X.device)
+    a = torch.empty((150,), dtype=torch.int32, device=X.device)
+    monkeypatch.setenv("ARCHEAD_TEST_ALLOC_LIMIT", "1024")
+    with pytest.raises(ArcheadError) as e:
+        h.forward_into(X, y, a)                 # M = 150 would grow the workspace
+    assert e.value.status == ENOMEM
+    h.forward_into(X[:2], y[:2], a[:2])         # fits the workspace it has
+    torch.cuda.synchronize()
+    ref = oracle_forward.forward(f, f["X"])
+    assert_logits_close(y[:2].cpu().numpy(), ref[:2], what="after a refused growth")
+    W = torch.randn(256, 128, dtype=torch.float64, device=X.device)
+    H = torch.randn(64, 128, dtype=torch.float64, device=X.device)
+    with pytest.raises(ArcheadError) as e:
+        build_head(W, H, 8, 4, 32)
+    assert e.value.status == ENOMEM
+    monkeypatch.delenv("ARCHEAD_TEST_ALLOC_LIMIT")
+    h.forward_into(X, y, a)
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    assert_logits_close(yy, ref, what="limit lifted")
+    assert_argmax_ok(a.cpu().numpy().astype(np.int64), yy, ref, what="limit lifted")
     h.close()

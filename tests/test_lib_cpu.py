@@ -143,3 +143,31 @@ def test_forward_sample_rejects_bad_temperature_and_missing_buffers(lib):
         assert lib.archead_forward_sample(None, 1, buf, 4, tau, buf, buf, buf, buf, buf, None) == binding.EINVAL
     assert lib.archead_forward_sample(None, 1, buf, 4, 1.0, None, buf, buf, buf, buf, None) == binding.EINVAL
     assert lib.archead_forward_sample(None, 1, buf, 4, 1.0, buf, buf, buf, buf, buf, None) == binding.EINVAL
+
+
+def test_pack_load_reports_enomem_under_the_allocation_limit(lib, monkeypatch):
+    """ARCHEAD_TEST_ALLOC_LIMIT refuses the packed head's device block before
+    any HIP call: a status, never an abort, and no handle."""
+    monkeypatch.setenv("ARCHEAD_TEST_ALLOC_LIMIT", "4096")
+    st, h = _load(lib, _fields())
+    assert st == binding.ENOMEM
+    assert h.value is None
+    assert b"ARCHEAD_TEST_ALLOC_LIMIT" in lib.archead_last_error()
+
+
+def test_build_reports_enomem_under_the_allocation_limit(lib, monkeypatch):
+    """The construction's first device allocation (the d x d metric) is refused
+    under the limit; the call returns ENOMEM without touching W or H."""
+    monkeypatch.setenv("ARCHEAD_TEST_ALLOC_LIMIT", "0")
+    V, d, k, r, g, N = 64, 128, 8, 4, 32, 16
+    dummy = np.zeros(8, dtype=np.float64)
+    bufs = {n: np.zeros(16, dtype=np.int8) for n in ["A5", "sA", "B8", "sB", "R4", "sR", "C8", "sC", "D8", "sD"]}
+    p = lambda n: bufs[n].ctypes.data
+    st = lib.archead_build(V, d, k, r, g, N, dummy.ctypes.data, dummy.ctypes.data, 0.75, 1e-2, 2, 16, 7,
+                           p("A5"), p("sA"), p("B8"), p("sB"), p("R4"), p("sR"), p("C8"), p("sC"), p("D8"),
+                           p("sD"), None)
+    assert st == binding.ENOMEM
+    assert b"device allocation" in lib.archead_last_error()
+    monkeypatch.setenv("ARCHEAD_TEST_ALLOC_LIMIT", "")
+    st = lib.archead_quantize(dummy.ctypes.data, 0, 8, 4, 8, p("A5"), p("sA"), None)
+    assert st == binding.OK or st == binding.EHIP  # no limit: the hook is off (rows = 0 launches nothing)
