@@ -173,17 +173,6 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
     auto sfrag = [&](int mt, int64_t ks, int h) -> u32x4 {
         return *(const u32x4 *)(s_ts + MT * kst * 1024 + (((mt * rst + ks) * 2 + h) * 64 + lane) * 8);
     };
-    // -144 sum_i t[m, i] per hidden state, once (the core codes are a + 144)
-    f32x4 nt[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        nt[mt] = zero;
-        for (int64_t ks = 0; ks < kst; ++ks) {
-            nt[mt] = mfma_bf16(tfrag(mt, ks, 0), neg144, nt[mt]);
-            nt[mt] = mfma_bf16(tfrag(mt, ks, 1), neg144, nt[mt]);
-        }
-    }
-
     // this wave's running top-1 key and (max, sum exp) per hidden state, in
     // LDS (the wave's own entries: no barrier), merged group by group
     for (int i = lane; i < MT * 16; i += 64) {
@@ -209,63 +198,97 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
             sa[v] = h2f(a.h.sa[vb[v] * kVB + lr]);
             sc[v] = h2f(a.h.sc[vb[v] * kVB + lr]);
         }
+        if constexpr (!XF) // the scale loads land here, not at a first use inside the stream
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
         // low-rank chunks: three core K-steps (A5 against t) or two
-        // correction K-steps (C8 against s); K-steps beyond the rank are skipped
+        // correction K-steps (C8 against s); K-steps beyond the rank are
+        // skipped.  Each chunk's sums are folded into acc with the row's
+        // scale (sA or sC) at the chunk's end, in passes of NH v-blocks: one
+        // chunk's sums and acc are all the low-rank phase holds besides the
+        // chunk buffers.
+        constexpr int NH = (MT == 2 && NV > 4) ? 3 : NV;
         {
-            f32x4 ga[NV][MT], gc[NV][MT];
+            // acc starts at sA (-144 sum_i t[m, i]): the core codes are a + 144
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x4 nt = zero;
+                for (int64_t ks = 0; ks < kst; ++ks) {
+                    nt = mfma_bf16(tfrag(mt, ks, 0), neg144, nt);
+                    nt = mfma_bf16(tfrag(mt, ks, 1), neg144, nt);
+                }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    ga[v][mt] = gc[v][mt] = zero;
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[v][mt][i] = sa[v] * nt[i];
+            }
             auto lr_chunk = [&](const u32x4(&q)[NV], int64_t c) __attribute__((always_inline)) {
-                if (c < na) {
+                const bool core = c < na;
+                // a correction chunk past the rank (the stream's padding) has no K-step
+                if (!core && 2 * (c - na) >= rst)
+                    return;
 #pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) {
-                        const int64_t ks = 3 * c + qq;
-                        if (ks >= kst)
-                            break;
-                        u32x4 th[MT], tl[MT];
+                for (int v0 = 0; v0 < NV; v0 += NH) {
+                    const int vn = v0 + NH < NV ? v0 + NH : NV;
+                    f32x4 g[NH][MT];
+                    if (core) {
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            th[mt] = tfrag(mt, ks, 0);
-                            tl[mt] = tfrag(mt, ks, 1);
+                        for (int qq = 0; qq < 3; ++qq) {
+                            const int64_t ks = 3 * c + qq;
+                            if (ks >= kst)
+                                break;
+                            u32x4 th[MT], tl[MT];
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) {
+                                th[mt] = tfrag(mt, ks, 0);
+                                tl[mt] = tfrag(mt, ks, 1);
+                            }
+#pragma unroll
+                            for (int v = v0; v < vn; ++v) {
+                                const uint32_t wn = qq == 0 ? q[v].x : qq == 1 ? q[v].y : q[v].z;
+                                const u32x4 b = a5_bf16_q(wn, q[v].w, qq);
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+                                    g[v - v0][mt] = mfma_bf16(tl[mt], b, mfma_bf16(th[mt], b, qq == 0 ? zero : g[v - v0][mt]));
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
+                    } else {
 #pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            const uint32_t wn = qq == 0 ? q[v].x : qq == 1 ? q[v].y : q[v].z;
-                            const u32x4 b = a5_bf16_q(wn, q[v].w, qq);
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int64_t ks = 2 * (c - na) + hh;
+                            if (ks >= rst)
+                                break;
+                            u32x4 sh[MT], sl[MT];
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt)
-                                ga[v][mt] = mfma_bf16(tl[mt], b, mfma_bf16(th[mt], b, ga[v][mt]));
+                            for (int mt = 0; mt < MT; ++mt) {
+                                sh[mt] = sfrag(mt, ks, 0);
+                                sl[mt] = sfrag(mt, ks, 1);
+                            }
+#pragma unroll
+                            for (int v = v0; v < vn; ++v) {
+                                u32x2 w;
+                                w.x = hh == 0 ? q[v].x : q[v].z;
+                                w.y = hh == 0 ? q[v].y : q[v].w;
+                                const u32x4 b = c8_bf16(w);
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt)
+                                    g[v - v0][mt] = mfma_bf16(sl[mt], b, mfma_bf16(sh[mt], b, hh == 0 ? zero : g[v - v0][mt]));
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        __builtin_amdgcn_sched_barrier(0);
                     }
-                } else {
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int64_t ks = 2 * (c - na) + hh;
-                        if (ks >= rst)
-                            break;
-                        u32x4 sh[MT], sl[MT];
+                    for (int v = v0; v < vn; ++v) {
+                        const float scl = core ? sa[v] : sc[v];
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            sh[mt] = sfrag(mt, ks, 0);
-                            sl[mt] = sfrag(mt, ks, 1);
-                        }
+                        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            u32x2 w;
-                            w.x = hh == 0 ? q[v].x : q[v].z;
-                            w.y = hh == 0 ? q[v].y : q[v].w;
-                            const u32x4 b = c8_bf16(w);
-#pragma unroll
-                            for (int mt = 0; mt < MT; ++mt)
-                                gc[v][mt] = mfma_bf16(sl[mt], b, mfma_bf16(sh[mt], b, gc[v][mt]));
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
+                            for (int i = 0; i < 4; ++i)
+                                acc[v][mt][i] = __builtin_fmaf(scl, g[v - v0][mt][i], acc[v][mt][i]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             };
             for (int64_t c = 0; c < nlr; c += kS2NB) {
@@ -277,18 +300,14 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // acc = sA (A5 t - 144 sum t) + sC (C8 s)
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[v][mt][i] = __builtin_fmaf(sa[v], ga[v][mt][i] + nt[mt][i], sc[v] * gc[v][mt][i]);
         }
 
         // residual K-chunks, slab by slab; each chunk is one g = 128 group,
-        // folded with its scale: acc += sR (sum x (q + 136) - 136 sum x)
+        // folded with its scale: acc += sR (sum x (q + 136) - 136 sum x),
+        // the group's sum starting from -136 sum x (the first product's C)
+        // every load older than the chunk stream's (the group's scales) has
+        // landed: said here, so that no wait for them is placed in the loop
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kS2NB * NV));
         for (int64_t s = 0; s < n_slab; ++s) {
             const int64_t S = j * n_slab + s;
             const uint16_t *xs_base;
@@ -299,48 +318,66 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
                 // chunk load: waiting for that chunk waits for the copy
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm((kS2NB - 1) * NV));
                 __syncthreads(); // every wave's part of slab S is in; slab S - 1 is done with
-                if (S + 1 < (int64_t)ngroups * n_slab)
-                    copy_slab(S + 1);
                 xs_base = s_x + (S & 1) * (MT * 16 * 512);
             }
 #pragma unroll
             for (int b = 0; b < kS2NB; ++b) {
                 const int64_t kc = s * kS2Slab + b;
-                f32x4 g[NV][MT];
+                if constexpr (!XF) { // the waves behind in the slab go first
+                    if (b == 0)
+                        __builtin_amdgcn_s_setprio(3);
+                    else if (b == 1)
+                        __builtin_amdgcn_s_setprio(2);
+                    else if (b == 2)
+                        __builtin_amdgcn_s_setprio(1);
+                    else
+                        __builtin_amdgcn_s_setprio(0);
+                }
+                // the chunk's v-blocks in passes of NH, each with its own group sums
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    u32x4 xf[MT];
+                for (int v0 = 0; v0 < NV; v0 += NH) {
+                    const int vn = v0 + NH < NV ? v0 + NH : NV;
+                    f32x4 xs[MT];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        xf[mt] = *(const u32x4 *)(xs_base + (((XF ? mt * nks : mt * 16) + b * 4 + st) * 64 + lane) * 8);
+                        xs[mt] = *(const f32x4 *)(s_xs + kc * (MT * 16) + mt * 16 + 4 * lq);
+                    f32x4 g[NH][MT];
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        const uint32_t wd = st == 0 ? buf[b][v].x : st == 1 ? buf[b][v].y
-                                            : st == 2 ? buf[b][v].z : buf[b][v].w;
-                        const u32x4 bb = r4_bf16(wd, kMagic);
+                    for (int st = 0; st < 4; ++st) {
+                        u32x4 xf[MT];
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
-                            g[v][mt] = mfma_bf16(xf[mt], bb, st == 0 ? zero : g[v][mt]);
+                            xf[mt] = *(const u32x4 *)(xs_base + (((XF ? mt * nks : mt * 16) + b * 4 + st) * 64 + lane) * 8);
+#pragma unroll
+                        for (int v = v0; v < vn; ++v) {
+                            const uint32_t wd = st == 0 ? buf[b][v].x : st == 1 ? buf[b][v].y
+                                                : st == 2 ? buf[b][v].z : buf[b][v].w;
+                            const u32x4 bb = r4_bf16(wd, kMagic);
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+                                g[v - v0][mt] = mfma_bf16(xf[mt], bb, st == 0 ? xs[mt] : g[v - v0][mt]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (vn == NV) { // the chunk's codes are used up: its slot takes the next item
+                        load_item(buf[b], jn, cn);
+                        advance();
+                        if constexpr (!XF)
+                            if (b == 0 && S + 1 < (int64_t)ngroups * n_slab)
+                                copy_slab(S + 1);
+                    }
+#pragma unroll
+                    for (int v = v0; v < vn; ++v) {
+                        const int64_t vrow = vb[v] - wg_lo;
+                        const float scl = h2f(s_sr[(vrow * G + kc) * kVB + lr]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                acc[v][mt][i] = __builtin_fmaf(scl, g[v - v0][mt][i], acc[v][mt][i]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                load_item(buf[b], jn, cn);
-                advance();
-                f32x4 xs[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    xs[mt] = *(const f32x4 *)(s_xs + kc * (MT * 16) + mt * 16 + 4 * lq);
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const int64_t vrow = vb[v] - wg_lo;
-                    const float scl = h2f(s_sr[(vrow * G + kc) * kVB + lr]);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[v][mt][i] = __builtin_fmaf(scl, g[v][mt][i] + xs[mt][i], acc[v][mt][i]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
