@@ -48,6 +48,7 @@ struct Stream2Args {
     float *logits; // M x V, may be null
     int want_argmax;
     int64_t nvb, nkc, G, na, nlr, kst, rst, kpad, rpad;
+    int64_t nlr_used; // low-rank chunks that carry K-steps (>= 1 when nlr > 0)
     int ngroups;   // groups of NV v-blocks per wave
     int n_slab;    // X slabs per group (nkc / kS2Slab)
     unsigned lds_x, lds_ts, lds_xs, lds_sr; // byte offsets of the LDS regions
@@ -146,12 +147,18 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
     const u32x4 *lrp = (const u32x4 *)a.h.lr;
     const u32x4 *r4p = (const u32x4 *)a.h.r4;
     u32x4 buf[kS2NB][NV];
+    // the low-rank chunks that carry K-steps; those past them pad the stream
+    // to a multiple of kS2NB and are never used: their slot reads the last
+    // used low-rank chunk again (same v-blocks, just read: a cache hit), so
+    // that every item still issues NV loads
+    const int64_t nlr_used = a.nlr_used;
     auto load_item = [&](u32x4(&q)[NV], int64_t j, int64_t c) __attribute__((always_inline)) {
         if (j >= ngroups) { // past the end: the last item again (never used)
             j = ngroups - 1;
             c = per - 1;
         }
-        const u32x4 *base = c < nlr ? lrp + c * nvb * 64 : r4p + (c - nlr) * nvb * 64;
+        const int64_t cl = c < nlr_used ? c : nlr_used - 1;
+        const u32x4 *base = c < nlr ? lrp + cl * nvb * 64 : r4p + (c - nlr) * nvb * 64;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             q[v] = __builtin_nontemporal_load(&base[vblock(j, v) * 64 + lane]);
@@ -545,6 +552,7 @@ hipError_t launch_vtile_stream2(const DevHead &h, const Work &w, const uint16_t 
     a.G = h.s.G();
     a.na = h.s.lr_na();
     a.nlr = (h.s.k + h.s.r) > 0 ? h.s.n_lr() : 0;
+    a.nlr_used = a.nlr > 0 ? h.s.lr_na() + h.s.lr_nc() : 0;
     a.kst = h.s.kst();
     a.rst = h.s.rst();
     a.kpad = h.s.kpad();
