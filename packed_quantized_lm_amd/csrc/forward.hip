@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a)
 constexpr int kPSmallM = 4; // largest M of the one-workgroup-per-column projection
 __global__ void proj_small_kernel(ProjArgs a);
 template <int MT>
-__global__ void proj_skinny_mfma_kernel(ProjArgs a);
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_skinny_mfma_kernel(ProjArgs a);
 
 static ProjArgs proj_args(const DevHead &h, const Work &w, const uint16_t *X)
 {
@@ -423,7 +423,7 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
 // output columns, K-slice): kProjKS slices of d, so that the grid's loads
 // (whose MFMA fragments touch 16 rows per instruction) spread over about
 // kProjKS times as many compute units as tiles.  Each wave issues its loads
-// up to eight K-steps at a time, stores its partial sums with device-scope
+// up to sixteen K-steps at a time, stores its partial sums with device-scope
 // stores and counts its tile; the last wave of a tile adds the slices in a
 // fixed order and writes t, s.  Integer weights enter as exact bf16
 // integers; each g-group of a D8 row is accumulated on its own and folded in
@@ -431,11 +431,11 @@ hipError_t launch_proj_mfma(const DevHead &h, const Work &w, const uint16_t *X, 
 // same sum).  Waves past the tiles write the per-group X sums, one row each,
 // from coalesced loads.
 // ---------------------------------------------------------------------------
-constexpr int kPSKB = 8;        // K-steps per load batch
+constexpr int kPSKB = 16;       // K-steps per load batch
 constexpr int kPSMaxD = 16384;  // widest d of the X-sum waves (their LDS row)
 
 template <int MT>
-__global__ __launch_bounds__(64) void proj_skinny_mfma_kernel(ProjArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_skinny_mfma_kernel(ProjArgs a)
 {
     const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     const int64_t ncol = a.k + a.r;
@@ -530,13 +530,17 @@ __global__ __launch_bounds__(64) void proj_skinny_mfma_kernel(ProjArgs a)
             }
         }
     }
-    // this slice's partial sums, complete before the tile's count
-    float *pp = a.ppart + ((tile * kProjKS + ks) * 2) * 256 + lane * 4;
+    // this slice's partial sums (pairs of floats as 64-bit device-scope
+    // stores), complete before the tile's count
+    uint64_t *pp = (uint64_t *)(a.ppart + ((tile * kProjKS + ks) * 2) * 256 + lane * 4);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(pp + mt * 256 + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int e = 0; e < 2; ++e)
+            __hip_atomic_store(pp + mt * 128 + e,
+                               (uint64_t)__float_as_uint(acc[mt][2 * e]) |
+                                   ((uint64_t)__float_as_uint(acc[mt][2 * e + 1]) << 32),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     uint32_t prev = 0;
     if (lane == 0)
@@ -546,32 +550,28 @@ __global__ __launch_bounds__(64) void proj_skinny_mfma_kernel(ProjArgs a)
     // the last slice of the tile: every slice's partials, in slice order
     if (lane == 0)
         __hip_atomic_store(a.pcnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // (pairs of floats as 64-bit device-scope loads; half of the slices at a
-    // time, all their loads in flight)
+    // (pairs of floats as 64-bit device-scope loads, all in flight at once)
     const uint64_t *tp = (const uint64_t *)(a.ppart + (tile * kProjKS * 2) * 256 + lane * 4);
     float v[MT][4];
+    uint64_t part[kProjKS][MT][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint64_t part[kProjKS / 2][MT][2];
+    for (int q = 0; q < kProjKS; ++q)
 #pragma unroll
-        for (int q = 0; q < kProjKS / 2; ++q)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int e = 0; e < 2; ++e)
+                part[q][mt][e] = __hip_atomic_load(tp + (q * 2 + mt) * 128 + e, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    part[q][mt][e] = __hip_atomic_load(tp + ((h * (kProjKS / 2) + q) * 2 + mt) * 128 + e,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < kProjKS; ++q)
 #pragma unroll
-        for (int q = 0; q < kProjKS / 2; ++q)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint64_t pr = part[q][mt][i >> 1];
-                    const float x = __uint_as_float((uint32_t)(i & 1 ? pr >> 32 : pr));
-                    v[mt][i] = (h == 0 && q == 0) ? x : v[mt][i] + x;
-                }
-    }
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t pr = part[q][mt][i >> 1];
+                const float x = __uint_as_float((uint32_t)(i & 1 ? pr >> 32 : pr));
+                v[mt][i] = q == 0 ? x : v[mt][i] + x;
+            }
     if (c0 + lr >= ncol)
         return;
     const float sb = isd ? 1.f : a.sb[c];

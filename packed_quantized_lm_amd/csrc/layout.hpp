@@ -139,7 +139,7 @@ struct Work {
     uint32_t *pcnt;         // [tiles]
 };
 
-constexpr int kProjKS = 16; // K-slices of the matrix-core projection for 5 <= M <= 32
+constexpr int kProjKS = 8; // K-slices of the matrix-core projection for 5 <= M <= 32
 
 constexpr int kDecodeMaxM = 2; // largest M of the single-launch decode path
 
