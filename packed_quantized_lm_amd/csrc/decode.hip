@@ -9,24 +9,22 @@
 //               + sA[v] sum_i A5[v,i] t[m,i] + sC[v] sum_i C8[v,i] s[m,i]   (a2)
 //   argmax[m] = lowest index of the row maximum                     (a3)
 //
-// One workgroup = 4 waves, each streaming a contiguous range of at most NV
-// v-blocks of 16 vocabulary rows (the ranges split the head evenly over
-// every slot of the grid).  A wave streams, for its v-blocks, every SC4
-// residual chunk and then every low-rank chunk (the chunk stream of
-// layout.hpp), two chunks per prefetch buffer and two buffers in flight.  Lane l works on row l % 16 of each
+// One workgroup = 4 waves x NV v-blocks of 16 vocabulary rows.  A wave
+// streams, for its v-blocks, every SC4 residual chunk and then every
+// low-rank chunk (the chunk stream of layout.hpp), two chunks per prefetch
+// buffer and two buffers in flight.  Lane l works on row l % 16 of each
 // v-block and on the 8 columns 8(l/16) .. +7 of each K-step, exactly the
 // lanes' share of the packed chunk: its codes become bf16 integer pairs by
 // exponent splicing and enter v_dot2_f32_bf16 against pairs of X (residual)
 // or of the bf16 hi/lo parts of t and s (low-rank).  The four lanes that
 // share a row meet by two shuffles at the end.
 //
-// a1 runs inside the same launch: the columns of t and s are spread over
-// the waves of the grid (projection-only workgroups where the grid leaves
-// slots free, else the streaming waves), each published through
-// device-scope stores followed by an increment of a counter.  The residual
-// needs none of it; three quarters through its residual a wave reads the
-// count once, and if every column is published it copies t and s to LDS,
-// and otherwise computes them itself.  No wave ever waits for another wave.
+// a1 runs inside the same launch: wave w of the grid computes columns w,
+// w + nw, ... of t and s (nw waves) and publishes them through device-scope
+// stores followed by an increment of a counter.  The residual needs none of
+// it; three quarters through its residual a wave reads the count once, and if
+// every column is published it copies t and s to LDS, and otherwise computes
+// them itself.  No wave ever waits for another wave.
 //
 // a3 runs inside it too: each workgroup folds its top-1 keys into 64-bit
 // atomic maxima, and the last workgroup to finish turns the keys into
@@ -188,32 +186,17 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     const bool proj_wg = (int)blockIdx.x < a.ntwg;
     __builtin_amdgcn_s_setprio(3); // lowered by the streaming waves as they go (pace below)
     const int64_t bid = (int64_t)blockIdx.x - a.ntwg; // streaming workgroup index
-    // the streaming waves split the v-blocks into contiguous ranges of at
-    // most NV (the host sizes the grid so): wave gw takes [lo(gw), lo(gw + 1))
-    const int64_t nwv = (int64_t)a.nwg * 4;
-    auto wave_lo = [&](int64_t g) -> int64_t { return g * nvb / nwv; };
-    const int64_t gw0 = proj_wg ? 0 : bid * 4 + wv;
-    const int64_t wg_vb0 = wave_lo(proj_wg ? 0 : bid * 4), wg_vb1 = wave_lo(proj_wg ? 0 : bid * 4 + 4);
-    const int64_t vlo = wave_lo(gw0), vhi = wave_lo(gw0 + 1);
+    const int64_t wg_vb0 = (proj_wg ? 0 : bid) * 4 * NV;
+    const int64_t vb0 = wg_vb0 + wv * NV;
     uint16_t *s_ts = (uint16_t *)(smem + a.lds_ts) + wv * (2 * MF * (kpad + rpad));
     uint32_t *const sync = a.w.sync;
     // the call's tag: column flags equal to it were written by this call
     const uint32_t epoch = __hip_atomic_load(sync + sync_epoch(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // slots past the range stream its last v-block again (or, for an empty
-    // range, a v-block of the workgroup) and produce nothing; sl[v] is the
-    // slot's v-block within the workgroup's staged scales
     int64_t vb[NV];
-    int sl[NV];
-    const int64_t vlast = vhi > vlo ? vhi - 1 : (wg_vb1 > wg_vb0 ? wg_vb1 - 1 : (vlo < nvb ? vlo : nvb - 1));
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        vb[v] = vlo + v < vhi ? vlo + v : vlast;
-        const int64_t r = vb[v] - wg_vb0;
-        sl[v] = (int)(r < 0 ? 0 : r < 4 * NV ? r : 4 * NV - 1);
-    }
-    // the row of lane lr in slot v, or V for a slot past the range
-    auto slot_row = [&](int v) -> int64_t { return vlo + v < vhi ? (vlo + v) * kVB + lr : V; };
+    for (int v = 0; v < NV; ++v)
+        vb[v] = vb0 + v < nvb ? vb0 + v : nvb - 1;
     // cross-entropy targets (uniform: scalar loads, complete long before use)
     int32_t tgt[MF];
 #pragma unroll
@@ -688,11 +671,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 const int it = t + 256 * i;
                 const int src = it / (NV * kVB);
                 const uint64_t wk = src < K ? s_win[src] : 0;
-                // the wave whose range holds the key's v-block, and its rows
-                const int64_t kb = (int64_t)((0xFFFFFFFFu - (uint32_t)wk) / kVB);
-                const int64_t gws = ((kb + 1) * nw - 1) / nvb;
-                const int64_t rr = wave_lo(gws) * kVB + (it - src * NV * kVB);
-                row[i] = (wk != 0 && rr < wave_lo(gws + 1) * kVB) ? rr : V;
+                const int64_t gws = (int64_t)((0xFFFFFFFFu - (uint32_t)wk) / kVB) / NV;
+                row[i] = wk != 0 ? gws * NV * kVB + (it - src * NV * kVB) : V;
                 y[i] = __hip_atomic_load(a.logits + m * V + (row[i] < V ? row[i] : 0), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -741,10 +721,8 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
 
     // Projection columns.  With projection-only workgroups, their wave pw
     // publishes columns pw, pw + 4 ntwg, ...; they start at once, stream
-    // nothing and leave.  Without them (every slot of the grid streams),
-    // the columns are spread evenly over the nw streaming waves, each wave
-    // publishing its share (at most one column at the Qwen shape) before its
-    // residual.
+    // nothing and leave.  Without them, streaming wave gw publishes columns
+    // gw, gw + nw, ... (nw streaming waves) before its residual.
     if (proj_wg) {
         const int64_t nx = MF * d / 8;
         for (int64_t i0 = 0; i0 < nx; i0 += 256) {
@@ -853,7 +831,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     {   // residual scales, row scales of the low-rank terms and X into LDS,
         // issued before the first prefetches so that the wait for them
         // leaves the prefetches in flight
-        const int64_t nvb_wg = wg_vb1 - wg_vb0; // at most 4 NV
+        const int64_t nvb_wg = (nvb - wg_vb0) < 4 * NV ? (nvb - wg_vb0) : 4 * NV;
         const int64_t nsr = nvb_wg * G * kVB / 8, nsa = nvb_wg * kVB / 8, nx = MF * d / 8;
         for (int64_t i0 = 0; i0 < nsr; i0 += 256) {
             const int64_t i = i0 + threadIdx.x;
@@ -881,11 +859,9 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     // outstanding; after the barrier, every wave's have
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NV));
     __syncthreads();
-    if (a.ntwg == 0) { // columns spread evenly over the streaming waves
-        const int64_t c0 = (gw * ntask + nw - 1) / nw, c1 = ((gw + 1) * ntask + nw - 1) / nw;
-        for (int64_t i = c0; i < c1; ++i)
+    if (a.ntwg == 0)
+        for (int64_t i = gw; i < ntask; i += nw)
             publish((int)i);
-    }
 
     // The offset of the residual codes, -136 sum_{j in grp} X[m,j], for
     // every group, once per wave: in the VALU variant each of the four lanes
@@ -940,7 +916,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             xo[m] = s_xs[m * G + kc];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const float scl = h2f(s_sr[(sl[v] * G + kc) * kVB + lr]);
+            const float scl = h2f(s_sr[((wv * NV + v) * G + kc) * kVB + lr]);
 #pragma unroll
             for (int m = 0; m < MF; ++m)
                 acc[v][m] = __builtin_fmaf(scl, gq[sel][v][m] + xo[m], acc[v][m]);
@@ -1003,7 +979,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
                 const int64_t grp = GS == 4 ? kc : ks / gsteps;
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    const float scl = h2f(s_sr[(sl[v] * G + grp) * kVB + lr]);
+                    const float scl = h2f(s_sr[((wv * NV + v) * G + grp) * kVB + lr]);
 #pragma unroll
                     for (int m = 0; m < MF; ++m) {
                         tot[v][m] = __builtin_fmaf(scl, g[v][m] + s_xs[m * G + grp], tot[v][m]);
@@ -1260,10 +1236,10 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
     for (; pi < nrp1 + nlp; pi += 2)
         lr_iter(pi);
     // tot += sA (A5 t - 144 sum t) + sC (C8 s)
-    const uint16_t *s_sa = (const uint16_t *)(smem + a.lds_sa);
+    const uint16_t *s_sa = (const uint16_t *)(smem + a.lds_sa) + wv * NV * kVB;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        const float sa = h2f(s_sa[sl[v] * kVB + lr]), sc = h2f(s_sa[4 * NV * kVB + sl[v] * kVB + lr]);
+        const float sa = h2f(s_sa[v * kVB + lr]), sc = h2f(s_sa[4 * NV * kVB + v * kVB + lr]);
         if constexpr (MX) {
 #pragma unroll
             for (int m = 0; m < MF; ++m)
@@ -1287,7 +1263,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         key[m] = 0;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        const int64_t row = slot_row(v);
+        const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
             float y;
@@ -1308,7 +1284,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             return;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int64_t row = slot_row(v);
+            const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
             for (int m = 0; m < MF; ++m)
                 if (row < V && lq == 0)
@@ -1338,7 +1314,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             float mx = -__builtin_inff();
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const int64_t row = slot_row(v);
+                const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
                 if (row < V) {
                     mx = fmaxf(mx, yv[v][m]);
                     if (row == tgt[m] && lane < 16)
@@ -1349,7 +1325,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
             float sx = 0.f;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const int64_t row = slot_row(v);
+                const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
                 if (row < V)
                     sx += exp_le0(yv[v][m] - mx);
             }
@@ -1366,7 +1342,7 @@ __global__ __launch_bounds__(256, 2) void gemv_decode_kernel(DecodeArgs a)
         const int64_t nw = (int64_t)a.nwg * 4;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int64_t row = slot_row(v);
+            const int64_t row = vb0 + v < nvb ? (vb0 + v) * kVB + lr : V;
 #pragma unroll
             for (int m = 0; m < MF; ++m)
                 if (row < V && lq == 0)
@@ -1419,25 +1395,13 @@ struct DecodeLds {
     size_t total;
 };
 
-// streaming workgroups of the single launch for M hidden states on n_cu
-// compute units: the slots of the grid (two workgroups per compute unit)
-// less room for (k + r) / 16 projection-only workgroups (four columns per
-// wave), so that the compute units get nearly the same number of v-blocks;
-// at least enough workgroups that no wave takes more than NV v-blocks, and
-// no more than one per 8 v-blocks (waves of two or more)
-static int64_t decode_nwg(const Shape &s, int64_t M, int n_cu)
-{
-    const int64_t nv = decode_nv((int)M), nvb = s.nvb();
-    const int64_t need = (nvb + 4 * nv - 1) / (4 * nv);
-    const int64_t pwg = (s.k + s.r + 15) / 16; // projection-only workgroups left room for: 4 columns per wave
-    const int64_t fill = std::min<int64_t>(int64_t(2) * n_cu - pwg, (nvb + 7) / 8);
-    return std::max(need, fill);
-}
+// streaming workgroups of the single launch for M hidden states
+static int64_t decode_nwg(const Shape &s, int64_t M) { return (s.nvb() + 4 * decode_nv((int)M) - 1) / (4 * decode_nv((int)M)); }
 
 // wave keys per thread of the last workgroup's top-k selection
-static int decode_tk_keys(const Shape &s, int64_t M, int n_cu) { return (int)((decode_nwg(s, M, n_cu) + 63) / 64); }
+static int decode_tk_keys(const Shape &s, int64_t M) { return (int)((decode_nwg(s, M) + 63) / 64); }
 
-static DecodeLds decode_lds(const Shape &s, int64_t M, int n_cu, int K = 0)
+static DecodeLds decode_lds(const Shape &s, int64_t M, int K = 0)
 {
     DecodeLds L;
     L.sa = (unsigned)dal16(size_t(4) * decode_nv((int)M) * s.G() * kVB * 2);
@@ -1447,7 +1411,7 @@ static DecodeLds decode_lds(const Shape &s, int64_t M, int n_cu, int K = 0)
     L.total = L.xs + size_t(4) * M * s.G() * 4;
     L.tk = (unsigned)dal16(L.total);
     if (K > 0)
-        L.total = L.tk + kTkMiscBytes + 256 * 8 + (size_t(4) * K * decode_tk_keys(s, M, n_cu) + kTkSpare) * 8 +
+        L.total = L.tk + kTkMiscBytes + 256 * 8 + (size_t(4) * K * decode_tk_keys(s, M) + kTkSpare) * 8 +
                   (size_t(K) * decode_nv((int)M) * kVB + kTkSpare) * 8;
     return L;
 }
@@ -1474,7 +1438,7 @@ static DecodeKernel decode_kernel(const DevHead &h, int64_t M, bool mx)
     // residual pairs and low-rank pairs each come in even counts (n_lr is a
     // multiple of 4 by construction); the matrix-core variant folds one
     // g = 128 group per K-chunk
-    if (M < 1 || M > kDecodeMaxM || h.s.nkc() % 4 != 0 || decode_lds(h.s, M, h.n_cu).total > 159 * 1024)
+    if (M < 1 || M > kDecodeMaxM || h.s.nkc() % 4 != 0 || decode_lds(h.s, M).total > 159 * 1024)
         return nullptr;
     const bool g128 = h.s.g == 4 * kKStep;
     if (mx) {
@@ -1497,8 +1461,8 @@ bool decode_ok(const DevHead &h, int64_t M, bool mx) { return decode_kernel(h, M
 
 bool decode_topk_ok(const DevHead &h, int64_t M, bool mx)
 {
-    return decode_ok(h, M, mx) && decode_tk_keys(h.s, M, h.n_cu) <= kTkKeys &&
-           decode_lds(h.s, M, h.n_cu, 16).total <= 72 * 1024; // two workgroups per compute unit
+    return decode_ok(h, M, mx) && decode_tk_keys(h.s, M) <= kTkKeys &&
+           decode_lds(h.s, M, 16).total <= 72 * 1024; // two workgroups per compute unit
 }
 
 int64_t decode_topk_keys(const Shape &s) { return int64_t(kDecodeMaxM) * ((s.nvb() + 15) / 16) * 16; }
@@ -1512,7 +1476,7 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     const int K = tk ? tk->K : 0;
     if (tk && (K < 1 || K > kTopKMax || !decode_topk_ok(h, w.M, mx)))
         return hipErrorInvalidValue;
-    const DecodeLds L = decode_lds(h.s, w.M, h.n_cu, K);
+    const DecodeLds L = decode_lds(h.s, w.M, K);
     DecodeArgs a;
     a.h = h;
     a.w = w;
@@ -1528,7 +1492,8 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     a.nlr = (h.s.k + h.s.r) > 0 ? h.s.n_lr() : 0;
     a.gsteps = (int)(h.s.g / kKStep);
     a.ntask = (int)(h.s.k + h.s.r);
-    a.nwg = (int)decode_nwg(h.s, w.M, h.n_cu);
+    const int nv = decode_nv((int)w.M);
+    a.nwg = (int)((a.nvb + 4 * nv - 1) / (4 * nv));
     // projection-only workgroups take the slots the streaming ones leave
     // free (two workgroups per CU), at least one column per wave
     const int64_t spare = int64_t(2) * h.n_cu - a.nwg;
@@ -1541,7 +1506,7 @@ hipError_t launch_decode(const DevHead &h, const Work &w, const uint16_t *X, flo
     a.lds_xs = L.xs;
     a.lds_tk = L.tk;
     a.tk_K = K;
-    a.tk_L = K ? decode_tk_keys(h.s, w.M, h.n_cu) : 0;
+    a.tk_L = K ? decode_tk_keys(h.s, w.M) : 0;
     a.tkw = w.tkp;
     a.tk_vals = tk ? tk->values : nullptr;
     a.tk_idx = tk ? tk->indices : nullptr;

@@ -1,13 +1,9 @@
 """Host emulation of the top-k selection fused into the single-launch decode
 kernel (csrc/decode.hip), with every lane, LDS and workspace index checked.
 
-Every streaming wave of the grid (4 per workgroup) takes a contiguous range
-of at most NV v-blocks of 16 rows -- wave g the v-blocks [lo(g), lo(g + 1)),
-lo(g) = g nvb / (4 nwg), with nwg the host's plan: every slot of the grid
-(two workgroups on each of 256 compute units) but those left to the
-projection, where that keeps waves at NV v-blocks or fewer and at two or
-more -- and leaves the largest key of its
-rows in the workspace, tkw[wave], and its logits in memory.  The last workgroup (256 threads) then
+Every streaming wave of the grid (4 per workgroup, NV v-blocks of 16 rows
+each) leaves the largest key of its rows in the workspace, tkw[wave], and its
+logits in memory.  The last workgroup (256 threads) then
   1. loads the wave keys, thread t keys t, t + 256, ... (Q of them);
   2. in each of its 4 waves takes the K-th largest of the 64 threads' maxima
      by ranking each against the other 63; the largest of the four is the
@@ -15,11 +11,9 @@ rows in the workspace, tkw[wave], and its logits in memory.  The last workgroup 
   3. gathers the wave keys at or above B into an LDS array of capacity
      4 K Q and ranks them: the K largest name the source waves, the K-th of
      them is T (0 with fewer than K nonzero wave keys);
-  4. reads the logits of the source waves -- the wave whose range holds a
-     key's v-block b is gws = ((b + 1) 4 nwg - 1) / nvb, its rows
-     lo(gws) 16 + i for i < NV 16 while below lo(gws + 1) 16 --, thread t
-     items t, t + 256, ... < SI 256, and gathers the keys at or above T into
-     an LDS array of capacity K NV 16;
+  4. reads the logits of the source waves, rows gws NV 16 + i (i < NV 16),
+     thread t items t, t + 256, ... < SI 256, and gathers the keys at or
+     above T into an LDS array of capacity K NV 16;
   5. ranks those: the K largest in order.
 Ranking n keys: with n <= 64 lane c of each wave compares key c with the
 keys j = wave mod 4 and the four partial ranks are added; with n <= 256
@@ -39,20 +33,6 @@ from oracle.select import top_k
 
 WAVES, LANES, NT, VB = 4, 64, 256, 16
 KMAX = 16
-N_CU = 256       # compute units of the part the plan is made for
-
-
-def plan_nwg(nvb, NV, ncol=320):
-    """Streaming workgroups of the single launch (decode_nwg) for a head with
-    ncol = k + r projection columns (room is left for ncol / 16
-    projection-only workgroups)."""
-    need = (nvb + WAVES * NV - 1) // (WAVES * NV)
-    fill = min(2 * N_CU - (ncol + 15) // 16, (nvb + 7) // 8)
-    return max(need, fill)
-
-
-def wave_lo(g, nvb, nw):
-    return g * nvb // nw
 SPARE = 8        # slots past each LDS array's capacity
 
 
@@ -119,7 +99,6 @@ def select_k(s, n, K):
 def resolve(y, tkw, NV, K, QMAX=12):
     """tkw: the wave keys of one hidden state (4 nwg of them); y: its logits."""
     V = y.size
-    nvb = (V + VB - 1) // VB
     nw = tkw.size
     Q = (nw // WAVES + 63) // 64
     assert 1 <= Q <= QMAX
@@ -163,11 +142,8 @@ def resolve(y, tkw, NV, K, QMAX=12):
             wk = win[src] if src < K else np.uint64(0)
             row = V
             if wk != 0:
-                kb = (0xFFFFFFFF - int(wk & np.uint64(0xFFFFFFFF))) // VB
-                gws = ((kb + 1) * nw - 1) // nvb
-                assert wave_lo(gws, nvb, nw) <= kb < wave_lo(gws + 1, nvb, nw)
-                rr = wave_lo(gws, nvb, nw) * VB + (it - src * NV * VB)
-                row = rr if rr < wave_lo(gws + 1, nvb, nw) * VB else V
+                gws = (0xFFFFFFFF - int(wk & np.uint64(0xFFFFFFFF))) // VB // NV
+                row = gws * NV * VB + (it - src * NV * VB)
             if row < V:
                 key = keys_of(y[row:row + 1], np.array([row]))[0]
                 if key >= T:
@@ -178,19 +154,16 @@ def resolve(y, tkw, NV, K, QMAX=12):
 
 
 def run_head(y, NV, K):
-    """y: the logits of one hidden state.  Emulates the grid: 4 waves per
-    workgroup, each with its range of v-blocks and its largest key."""
+    """y: the logits of one hidden state.  Emulates the grid: 4 waves x NV
+    v-blocks of 16 rows per workgroup, each wave's largest key."""
     V = y.size
     nvb = (V + VB - 1) // VB
-    nwg = plan_nwg(nvb, NV)
-    nw = nwg * WAVES
-    tkw = np.zeros(nw, dtype=np.uint64)
+    nwg = (nvb + WAVES * NV - 1) // (WAVES * NV)
+    tkw = np.zeros(nwg * WAVES, dtype=np.uint64)
     allkeys = keys_of(y, np.arange(V))
-    for gw in range(nw):
-        lo, hi = wave_lo(gw, nvb, nw), wave_lo(gw + 1, nvb, nw)
-        assert hi - lo <= NV
-        r0, r1 = lo * VB, min(hi * VB, V)
-        tkw[gw] = allkeys[r0:r1].max() if r0 < r1 else 0
+    for gw in range(nwg * WAVES):
+        r0, r1 = gw * NV * VB, min((gw + 1) * NV * VB, V)
+        tkw[gw] = allkeys[r0:r1].max() if r0 < V else 0
     return resolve(y, tkw, NV, K)
 
 
@@ -271,7 +244,7 @@ def test_wave_key_ranking_beyond_one_per_thread():
 
 
 def test_candidates_are_few_at_the_qwen_shape():
-    """At V = 151936 with NV = 5 (1968 waves, 8 wave keys per thread) random
+    """At V = 151936 with NV = 5 (1900 waves, 8 wave keys per thread) random
     logits leave a handful of wave keys and candidate rows."""
     rng = np.random.default_rng(9)
     V, NV, K = 151936, 5, 16
