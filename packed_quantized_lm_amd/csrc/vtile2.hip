@@ -22,10 +22,10 @@
 // reads are free of bank conflicts.  t and s are staged once.  Where all of
 // X fits beside them (one m-tile and d up to about 2560), X is staged once
 // too and the stream has no barrier; otherwise X is staged in slabs of four
-// K-chunks (512 columns), two slab buffers, the next slab's copy issued a
-// whole slab ahead by the eight waves together and checked at the slab
-// boundary by one wait (the copy is older than the chunk the wave needs
-// next) and one barrier.  The only other vector-memory loads of the loop
+// K-chunks (512 columns), two slab buffers, the next slab's copy issued by
+// the eight waves together after their first chunk of the current slab and
+// checked at the slab boundary by one wait (three chunks' loads were issued
+// after it) and one barrier.  The only other vector-memory loads of the loop
 // are the packed codes.
 #include <hip/hip_runtime.h>
 
@@ -321,8 +321,10 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
             if constexpr (XF) {
                 xs_base = s_x + s * 16 * 512; // K-step 16 s of m-tile 0 (m-tile mt: + mt nks blocks)
             } else {
-                // the copy of slab S was issued before the oldest outstanding
-                // chunk load: waiting for that chunk waits for the copy
+                // the copy of slab S went out right after the first chunk
+                // reload of the slab before it (at the start, for slab 0):
+                // at least (kS2NB - 1) NV chunk loads were issued after it, so
+                // with at most that many outstanding the copy has landed
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm((kS2NB - 1) * NV));
                 __syncthreads(); // every wave's part of slab S is in; slab S - 1 is done with
                 xs_base = s_x + (S & 1) * (MT * 16 * 512);
