@@ -19,7 +19,8 @@
 // bf16 integers, device.hpp).  The A operands -- X, and the bf16 hi/lo parts
 // of t and s -- are read from LDS, where they sit in MFMA fragment order (one
 // 1 KiB block per 16 rows x 32 columns: lane l's 16 bytes at 16 l), so the
-// reads are free of bank conflicts.  t and s are staged once.  Where all of
+// reads are free of bank conflicts.  t and s, and the workgroup's residual
+// and row scales, are staged once.  Where all of
 // X fits beside them (one m-tile and d up to about 2560), X is staged once
 // too and the stream has no barrier; otherwise X is staged in slabs of four
 // K-chunks (512 columns), two slab buffers, the next slab's copy issued by
@@ -40,6 +41,9 @@ constexpr int kS2Waves = 8;  // waves per workgroup, one workgroup per compute u
 constexpr int kS2Slab = 4;   // residual K-chunks per X slab
 constexpr int kS2NB = 4;     // chunks in flight per wave
 constexpr int kS2MaxM = 32;
+// dynamic LDS of a workgroup: 160 KiB less the kernel's static arrays (at
+// most 4.3 KiB at two m-tiles) and a margin
+constexpr size_t kS2Lds = 154 * 1024;
 
 struct Stream2Args {
     DevHead h;
@@ -51,7 +55,7 @@ struct Stream2Args {
     int64_t nlr_used; // low-rank chunks that carry K-steps (>= 1 when nlr > 0)
     int ngroups;   // groups of NV v-blocks per wave
     int n_slab;    // X slabs per group (nkc / kS2Slab)
-    unsigned lds_x, lds_ts, lds_xs, lds_sr; // byte offsets of the LDS regions
+    unsigned lds_x, lds_ts, lds_xs, lds_sr, lds_sa; // byte offsets of the LDS regions
 };
 
 // v-block range [lo, hi) of wave gw of W
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
     uint16_t *const s_ts = (uint16_t *)(smem + a.lds_ts); // t [MT][kst][2][64][8], then s [MT][rst][2][64][8]
     float *const s_xs = (float *)(smem + a.lds_xs);       // [G][MT*16]  -136 sum of X over the group
     uint16_t *const s_sr = (uint16_t *)(smem + a.lds_sr); // [v-blocks of the workgroup][G][16] fp16
+    uint16_t *const s_sa = (uint16_t *)(smem + a.lds_sa); // [v-blocks of the workgroup][16] sA, then the same for sC
 
     const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,6 +103,16 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
         for (int64_t i0 = wv * 64; i0 < nsr; i0 += kS2Waves * 64)
             if (i0 + lane < nsr)
                 lds_dma16<false>(src + i0 + lane, (u32x4 *)s_sr + i0);
+        // the rows' sA and sC, read at each group's start: from LDS, a read
+        // there waits for no chunk load in flight
+        const int64_t nsa = (wg_hi - wg_lo) * kVB / 8; // 16-byte pieces of each
+        const u32x4 *sa_src = (const u32x4 *)(a.h.sa + wg_lo * kVB);
+        const u32x4 *sc_src = (const u32x4 *)(a.h.sc + wg_lo * kVB);
+        for (int64_t i0 = wv * 64; i0 < 2 * nsa; i0 += kS2Waves * 64) {
+            const int64_t i = i0 + lane;
+            if (i < 2 * nsa)
+                lds_dma16<false>(i < nsa ? sa_src + i : sc_src + (i - nsa), (u32x4 *)s_sa + i0);
+        }
         // -136 sum of X per group: xs[grp][j] = xsneg[grp][j]
         const int64_t nxs = G * MT * 16;
         for (int64_t i0 = wv * 64; i0 < nxs; i0 += kS2Waves * 64) {
@@ -202,11 +217,9 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             vb[v] = vblock(j, v);
-            sa[v] = h2f(a.h.sa[vb[v] * kVB + lr]);
-            sc[v] = h2f(a.h.sc[vb[v] * kVB + lr]);
+            sa[v] = h2f(s_sa[(vb[v] - wg_lo) * kVB + lr]);
+            sc[v] = h2f(s_sa[(wg_hi - wg_lo + vb[v] - wg_lo) * kVB + lr]);
         }
-        if constexpr (!XF) // the scale loads land here, not at a first use inside the stream
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
         // low-rank chunks: three core K-steps (A5 against t) or two
         // correction K-steps (C8 against s); K-steps beyond the rank are
@@ -312,8 +325,8 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
         // residual K-chunks, slab by slab; each chunk is one g = 128 group,
         // folded with its scale: acc += sR (sum x (q + 136) - 136 sum x),
         // the group's sum starting from -136 sum x (the first product's C)
-        // every load older than the chunk stream's (the group's scales) has
-        // landed: said here, so that no wait for them is placed in the loop
+        // no load older than the chunk stream's is outstanding: said here,
+        // so that no wait for one is placed in the loop
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(kS2NB * NV));
         for (int64_t s = 0; s < n_slab; ++s) {
             const int64_t S = j * n_slab + s;
@@ -471,7 +484,7 @@ __global__ __launch_bounds__(kS2Waves * 64, 1) void vtile_stream2_kernel(Stream2
 struct Stream2Plan {
     bool ok, xfull;
     int MT, NV, nwg, ngroups;
-    unsigned lds_x, lds_ts, lds_xs, lds_sr;
+    unsigned lds_x, lds_ts, lds_xs, lds_sr, lds_sa;
     size_t lds;
 };
 
@@ -500,17 +513,20 @@ Stream2Plan stream2_plan(const DevHead &h, int64_t M)
     const size_t xs_bytes = size_t(s.G()) * p.MT * 16 * 4;
     // the workgroup's v-block range holds at most 8 per_wave v-blocks
     const size_t sr_bytes = size_t(kS2Waves) * per_wave * s.G() * kVB * 2;
-    const size_t rest = al256(ts_bytes) + al256(xs_bytes) + al256(sr_bytes);
+    // and sA, sC of those rows
+    const size_t sa_bytes = size_t(2) * kS2Waves * per_wave * kVB * 2;
+    const size_t rest = al256(ts_bytes) + al256(xs_bytes) + al256(sr_bytes) + al256(sa_bytes);
     // all of X in LDS where it fits (no barrier in the stream), else two slabs
     const size_t x_full = size_t(p.MT) * (s.d / kKStep) * 1024, x_slabs = size_t(2) * p.MT * 16 * 1024;
-    p.xfull = al256(x_full) + rest <= 150 * 1024;
+    p.xfull = al256(x_full) + rest <= kS2Lds;
     const size_t x_bytes = p.xfull ? x_full : x_slabs;
     p.lds_x = 0;
     p.lds_ts = (unsigned)al256(x_bytes);
     p.lds_xs = (unsigned)(p.lds_ts + al256(ts_bytes));
     p.lds_sr = (unsigned)(p.lds_xs + al256(xs_bytes));
-    p.lds = p.lds_sr + al256(sr_bytes);
-    if (p.lds > 150 * 1024)
+    p.lds_sa = (unsigned)(p.lds_sr + al256(sr_bytes));
+    p.lds = p.lds_sa + al256(sa_bytes);
+    if (p.lds > kS2Lds)
         p.ok = false;
     return p;
 }
@@ -565,6 +581,7 @@ hipError_t launch_vtile_stream2(const DevHead &h, const Work &w, const uint16_t 
     a.lds_ts = p.lds_ts;
     a.lds_xs = p.lds_xs;
     a.lds_sr = p.lds_sr;
+    a.lds_sa = p.lds_sa;
     if (p.MT == 1 && p.xfull)
         return p.NV == 5 ? launch2<1, 5, true>(a, p, st) : launch2<1, 4, true>(a, p, st);
     if (p.MT == 1)
