@@ -14,16 +14,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "packed_quantized_lm_amd", "csrc")
 
 
-def _resource_usage(src):
+def _compile(src, asm=False):
+    """(resource usage per kernel, device assembly or None) of one source."""
     from packed_quantized_lm_amd import build as b
     hipcc = os.path.join(b.ROCM, "bin", "hipcc")
     if not os.path.exists(hipcc) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
-    cmd = [hipcc, *b.HIP_FLAGS, f"-I{b.INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+    out_args = ["--cuda-device-only", "-S", "-o", "-"] if asm else ["-c", "-o", os.devnull]
+    cmd = [hipcc, *b.HIP_FLAGS, f"-I{b.INCLUDE}", f"-I{CSRC}", os.path.join(CSRC, src), *out_args,
            "-Rpass-analysis=kernel-resource-usage"]
-    out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, check=True).stdout
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, check=True)
     usage, name = {}, None
-    for line in out.splitlines():
+    for line in (p.stderr + "\n" + (p.stdout if not asm else "")).splitlines():
         m = re.search(r"Function Name: (\S+)", line)
         if m:
             name = m.group(1)
@@ -32,26 +34,16 @@ def _resource_usage(src):
         m = re.search(r"remark: +([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
         if m and name:
             usage[name][m.group(1).strip()] = int(m.group(2))
-    return usage
+    return usage, (p.stdout if asm else None)
 
 
 def test_single_launch_decode_instances_do_not_spill():
-    usage = _resource_usage("decode.hip")
+    usage, _ = _compile("decode.hip")
     kernels = {n: u for n, u in usage.items() if "gemv_decode_kernel" in n}
     assert len(kernels) == 4, sorted(usage)
     for n, u in kernels.items():
         assert u.get("ScratchSize", -1) == 0, f"{n} spills: {u}"
         assert u.get("Occupancy", 0) >= 2, f"{n}: {u}"
-
-
-def _device_asm(src):
-    from packed_quantized_lm_amd import build as b
-    hipcc = os.path.join(b.ROCM, "bin", "hipcc")
-    if not os.path.exists(hipcc) and not shutil.which("hipcc"):
-        pytest.skip("hipcc not available")
-    cmd = [hipcc, *b.HIP_FLAGS, f"-I{b.INCLUDE}", f"-I{CSRC}", "--cuda-device-only", "-S",
-           os.path.join(CSRC, src), "-o", "-"]
-    return subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, check=True).stdout
 
 
 def test_batched_decode_instances_keep_their_prefetches_in_flight():
@@ -63,12 +55,11 @@ def test_batched_decode_instances_keep_their_prefetches_in_flight():
     memory access (s_waitcnt vmcnt(0)): a load whose first use follows it at
     once -- such as a scale read from global memory at a group's start --
     would place one there and empty the prefetch queue."""
-    usage = _resource_usage("vtile2.hip")
+    usage, asm = _compile("vtile2.hip", asm=True)
     kernels = {n: u for n, u in usage.items() if "vtile_stream2_kernel" in n}
     assert len(kernels) == 8, sorted(usage)
     for n, u in kernels.items():
         assert u.get("ScratchSize", -1) == 0, f"{n} spills: {u}"
-    asm = _device_asm("vtile2.hip")
     bodies = re.findall(r"^(_Z\w*vtile_stream2_kernel\w*):(.*?)\.end_amdhsa_kernel", asm, re.S | re.M)
     assert len(bodies) == 8, [b[0] for b in bodies]
     for name, body in bodies:
